@@ -47,19 +47,24 @@ def _tiles(N, bq, bkv):
     return Tq, Tk, rows_valid.astype(np.int64), cols_valid.astype(np.int64), pad_col
 
 
-def tile_counts(F, H, W, kind, sink_frames, spatial_band, temporal_band, temporal_layout, bq, bkv):
+def tile_counts(F, H, W, kind, sink_frames, spatial_band, temporal_band, temporal_layout, bq, bkv, q_tiles=None):
     """c[I, J] = retained (query, key) pairs of tile (I, J), valid rows and columns only.
 
     Element scan: for every query row of tile I, the keep rule is evaluated
     against every key of the sequence (in executed order); the Booleans are
-    then summed per key tile.
+    then summed per key tile. ``q_tiles`` restricts the scan to those query
+    tiles; the other rows of the result are -1.
     """
     N = F * H * W
     order = executed_order(F, H, W, kind, sink_frames, temporal_layout)
     Tq, Tk, _, _, _ = _tiles(N, bq, bkv)
     c = np.zeros((Tq, Tk), dtype=np.int64)
+    tiles = range(Tq)
+    if q_tiles is not None:
+        c[:] = -1
+        tiles = sorted(set(int(i) for i in q_tiles))
     buf = np.zeros((bq, Tk * bkv), dtype=bool)
-    for I in range(Tq):
+    for I in tiles:
         rows = order[I * bq:min(N, (I + 1) * bq)]
         keep = head_keep_block(kind, F, H, W, sink_frames, spatial_band, temporal_band, rows, order)
         r = rows.size

@@ -1,0 +1,184 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+75,600 tokens (21 x 45 x 80), 10 heads (5 spatial band 4 + 5 temporal window
+644, first-frame sink), head dim 128, bf16, tiles 256 x 128; and the
+302,400-token (21 x 90 x 160) routing workload. The oracle computes sampled
+rows one by one (each row's softmax over all 75,600 or 302,400 keys), plus
+every row of the first and last query tiles.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_spatio_amd as B
+import oracle as O
+from synth import HEADLINE, P1440, normal_qkv, planted_qkv, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def geom_mask(w):
+    return (w.F, w.H, w.W), (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+
+
+def sample_rows(N, bq, n, seed):
+    r = np.random.default_rng(seed).choice(N, n, replace=False)
+    return np.unique(np.concatenate([r, np.arange(64), np.arange(N - 64, N), np.arange(bq - 16, bq + 16)]))
+
+
+@pytest.fixture(scope="module")
+def headline(dev):
+    w = HEADLINE
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=0)
+    return w, q, k, v, q.to(dev), k.to(dev), v.to(dev)
+
+
+def pipeline(dev, w, qd, kd, vd, flags, bq, bkv, mode, gather=False):
+    geom, mask = geom_mask(w)
+    tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
+    if gather:
+        o, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, bq, bkv, mode, gather_temporal=True)
+        return o
+    qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (qd, kd, vd))
+    op, _ = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode)
+    return B.svga_unpermute(op, flags, geom, mask)
+
+
+@pytest.mark.parametrize("bq", [128, 256, 512])
+def test_headline_device_tilemaps(dev, bq):
+    w = HEADLINE
+    geom, mask = geom_mask(w)
+    for mode in range(4):
+        say(f"headline tilemap bq={bq} mode={mode}")
+        d = B.svga_build_tilemap(geom, mask, bq, 128, mode, device=dev).cpu().numpy()
+        h = B.svga_build_tilemap_host(geom, mask, bq, 128, mode)
+        assert np.array_equal(d, h)
+
+
+@pytest.mark.parametrize("mode,bq", [(B.MAP_EXACT, 256), (B.MAP_ROUNDED, 128), (B.MAP_DENSE, 256), (B.MAP_EXACT, 128)])
+def test_headline_sampled_rows(dev, headline, mode, bq):
+    w, q, k, v, qd, kd, vd = headline
+    geom, mask = geom_mask(w)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say(f"headline attention mode={mode} bq={bq}")
+    o = pipeline(dev, w, qd, kd, vd, flags, bq, 128, mode).cpu()
+    scale = 1 / math.sqrt(w.d)
+    for h, kind in enumerate(w.kinds):
+        rows = sample_rows(w.N, bq, 96, seed=h)
+        cls_r = None
+        if mode == B.MAP_ROUNDED:
+            # oracle element scan of just the query tiles that hold the sampled rows
+            order = O.executed_order(w.F, w.H, w.W, kind, mask[0], mask[3])
+            pos = np.empty_like(order)
+            pos[order] = np.arange(order.size)
+            counts = O.tile_counts(w.F, w.H, w.W, kind, *mask[:3], mask[3], bq, 128, q_tiles=pos[rows] // bq)
+            cls_r = O.classify(w.F, w.H, w.W, kind, *mask[:3], mask[3], bq, 128, O.MODE_ROUNDED,
+                               counts=counts)["cls"]
+        ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(), kind,
+                                  w.F, w.H, w.W, *mask[:3], mask[3], mode, bq, 128, scale, rows=rows,
+                                  cls_rounded=cls_r)
+        got = o[0, h, rows].double().numpy()
+        err = np.abs(got - ref)
+        say(f"  head {h} kind {kind}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (|ref| max {np.abs(ref).max():.3f})")
+        assert np.isfinite(got).all()
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
+def test_headline_sharpened_scores(dev, headline):
+    """Q scaled by 8: peaked softmax, O(1) outputs, so the absolute bound is tight."""
+    w, q, k, v, qd, kd, vd = headline
+    geom, mask = geom_mask(w)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    q8 = (q.float() * 8).to(torch.bfloat16)
+    say("headline sharpened")
+    o = pipeline(dev, w, q8.to(dev), kd, vd, flags, 256, 128, B.MAP_EXACT).cpu()
+    for h in (0, 7):
+        rows = sample_rows(w.N, 256, 64, seed=10 + h)
+        ref, _ = O.attention_head(q8[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                                  w.kinds[h], w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, 256, 128,
+                                  1 / math.sqrt(w.d), rows=rows)
+        err = np.abs(o[0, h, rows].double().numpy() - ref)
+        say(f"  head {h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (|ref| max {np.abs(ref).max():.3f})")
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
+def test_headline_census(dev):
+    """Q = 0, V[k, c] = [k mod 128 == c]: each output is the exact share of the row's kept keys in a
+    residue class; one missing or extra 128-key tile shifts a column by about 1/|row| relative."""
+    w = HEADLINE
+    geom, mask = geom_mask(w)
+    N, d = w.N, w.d
+    say("headline census")
+    qd = torch.zeros(1, w.heads, N, d, dtype=torch.bfloat16, device=dev)
+    vd = torch.zeros(1, w.heads, N, d, dtype=torch.bfloat16, device=dev)
+    idx = torch.arange(N, device=dev)
+    vd[:, :, idx, idx % d] = 1
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    o = pipeline(dev, w, qd, qd, vd, flags, 256, 128, B.MAP_EXACT).float().cpu().numpy()
+    t = np.arange(N)
+    for h, kind in enumerate(w.kinds):
+        rows = sample_rows(N, 256, 48, seed=20 + h)
+        keep = O.head_keep_block(kind, w.F, w.H, w.W, *mask[:3], rows, t)
+        for n, r in enumerate(rows):
+            kept = t[keep[n]]
+            want = np.bincount(kept % d, minlength=d) / kept.size
+            rel = np.abs(o[0, h, r] - want) / want
+            assert rel.max() < 2 ** -7, (h, r, rel.max())
+
+
+def test_headline_gather_equals_permute_bitwise(dev, headline):
+    w, q, k, v, qd, kd, vd = headline
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say("headline gather vs permute")
+    a = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT)
+    b = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT, gather=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_1440p_routing_and_attention(dev):
+    """Routing on 64 sampled queries at 302,400 tokens finds the planted head kinds; the routed
+    pipeline matches the oracle on sampled rows."""
+    w = P1440
+    geom, mask = geom_mask(w)
+    say("1440p inputs")
+    q, k, v = planted_qkv(1, w.F, w.H, w.W, w.d, w.kinds, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    idx = sample_indices(w.N, 64, seed=0)
+    say("1440p routing")
+    flags, err = B.svga_route_heads(qd, kd, vd, geom, mask, idx.to(dev))
+    f = flags.cpu().numpy()
+    e = err.cpu().numpy()
+    say(f"  flags {f.tolist()}")
+    scale = 1 / math.sqrt(w.d)
+    for h in (0, 5, 9):
+        fr, er = O.route_heads(q[:, h:h + 1].double().numpy(), k[:, h:h + 1].double().numpy(),
+                               v[:, h:h + 1].double().numpy(), w.F, w.H, w.W, *mask[:3], idx.numpy(), scale)
+        say(f"  head {h}: gpu err {e[0, h].tolist()} oracle {er[0, 0].tolist()}")
+        assert np.abs(e[0, h] - er[0, 0]).max() <= 1e-3 * er[0, 0].max()
+        assert f[0, h] == fr[0, 0]
+    assert tuple(f[0]) == w.kinds
+    say("1440p attention")
+    o = pipeline(dev, w, qd, kd, vd, flags, w.bq, w.bkv, B.MAP_EXACT).cpu()
+    for h in (1, 8):
+        rows = sample_rows(w.N, w.bq, 32, seed=30 + h)
+        ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                                  w.kinds[h], w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, w.bq, w.bkv, scale,
+                                  rows=rows)
+        err = np.abs(o[0, h, rows].double().numpy() - ref)
+        say(f"  head {h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS

@@ -1,0 +1,312 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle, at sizes the oracle finishes in seconds.
+
+Bars: tile maps and permutations bit-exact; bf16 attention outputs within
+max-abs 2e-2 and mean-abs 2e-3 of the fp64 oracle (plus exact-rational census
+checks); routing errors within 1e-3 relative, flags equal except near-ties.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_spatio_amd as B
+import oracle as O
+from synth import SMALL, TINY, census_qkv, normal_qkv, planted_qkv, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def i16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy()
+
+
+def run_attention(dev, geom, mask, q, k, v, kinds, bq, bkv, mode, gather=False, want_lse=False):
+    """Frame-major in, frame-major out: permute -> attention -> unpermute (or the in-kernel gather)."""
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    Bn = q.shape[0]
+    flags = torch.tensor([list(kinds)] * Bn, dtype=torch.uint8, device=dev)
+    tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
+    if gather:
+        o, lse = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, bq, bkv, mode, gather_temporal=True,
+                                        want_lse=want_lse)
+    else:
+        qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (qd, kd, vd))
+        op, lsep = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode, want_lse=want_lse)
+        o = B.svga_unpermute(op, flags, geom, mask)
+        lse = None
+        if want_lse:
+            # LSE rows follow the executed order; bring temporal heads back to frame-major
+            lse = lsep.clone()
+            for h, kind in enumerate(kinds):
+                if kind:
+                    order = torch.from_numpy(O.executed_order(geom[0], geom[1], geom[2], 1, mask[0], mask[3])).to(dev)
+                    lse[:, h, order] = lsep[:, h]
+    torch.cuda.synchronize()
+    return o.cpu(), (lse.cpu() if lse is not None else None)
+
+
+def oracle_head(geom, mask, q, k, v, kind, mode, bq, bkv, scale, rows=None):
+    F, H, W = geom
+    sink, bs, bt, lay = mask
+    cls_r = None
+    if mode == O.MODE_ROUNDED:
+        cls_r = O.classify(F, H, W, kind, sink, bs, bt, lay, bq, bkv, O.MODE_ROUNDED)["cls"]
+    return O.attention_head(q.double().numpy(), k.double().numpy(), v.double().numpy(), kind, F, H, W, sink, bs,
+                            bt, lay, mode, bq, bkv, scale, rows=rows, cls_rounded=cls_r)
+
+
+def assert_close(got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    say(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert np.isfinite(got).all(), what
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS, what
+
+
+# ---------------------------------------------------------------- tile maps
+
+@pytest.mark.parametrize("w", [TINY, SMALL], ids=["tiny", "small"])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("lay", [0, 1])
+def test_device_tilemap_equals_host(dev, w, mode, lay):
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, lay)
+    say(f"tilemap {w.name} mode={mode} layout={lay}")
+    for bq, bkv in ((w.bq, w.bkv), (64, 32), (32, 64)):
+        d = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev).cpu().numpy()
+        h = B.svga_build_tilemap_host(geom, mask, bq, bkv, mode)
+        assert np.array_equal(d, h), (bq, bkv)
+
+
+def test_device_tilemap_random_geometries(dev):
+    rng = np.random.default_rng(9)
+    for it in range(40):
+        F, H, W = (int(x) for x in rng.integers(1, 12, 3))
+        sink = int(rng.integers(0, F + 1))
+        mask = (sink, int(rng.integers(0, F + 1)), int(rng.integers(0, H * W + 2)), int(rng.integers(0, 2)))
+        bq, bkv = int(rng.choice([1, 3, 16, 32, 64, 128])), int(rng.choice([1, 5, 16, 32, 64, 128]))
+        mode = int(rng.integers(0, 4))
+        say(f"tilemap random #{it}: geom={(F, H, W)} mask={mask} tiles={bq}x{bkv} mode={mode}")
+        d = B.svga_build_tilemap((F, H, W), mask, bq, bkv, mode, device=dev).cpu().numpy()
+        h = B.svga_build_tilemap_host((F, H, W), mask, bq, bkv, mode)
+        assert np.array_equal(d, h)
+
+
+# ---------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("geom", [(4, 4, 8), (9, 16, 24), (5, 3, 7), (3, 1, 1)])
+@pytest.mark.parametrize("sink", [0, 1, 2])
+@pytest.mark.parametrize("lay", [0, 1])
+@pytest.mark.parametrize("d", [64, 128, 8])
+def test_permute_unpermute_bitwise(dev, geom, sink, lay, d):
+    F, H, W = geom
+    sink = min(sink, F)
+    N = F * H * W
+    mask = (sink, 1, 2, lay)
+    kinds = (0, 1, 1, 0, 1)
+    say(f"permute geom={geom} sink={sink} layout={lay} d={d}")
+    x = torch.randn(2, len(kinds), N, d).to(torch.bfloat16)
+    flags = torch.tensor([kinds, kinds[::-1]], dtype=torch.uint8, device=dev)
+    xd = x.to(dev)
+    xp = B.svga_permute(xd, flags, geom, mask)
+    back = B.svga_unpermute(xp, flags, geom, mask)
+    torch.cuda.synchronize()
+    order = O.executed_order(F, H, W, O.KIND_TEMPORAL, sink, lay)
+    xn = i16(x)
+    want = xn.copy()
+    fl = flags.cpu().numpy()
+    for b in range(2):
+        for h in range(len(kinds)):
+            if fl[b, h]:
+                want[b, h] = O.permute(xn[b, h], order)
+    assert np.array_equal(i16(xp), want)
+    assert np.array_equal(i16(back), xn)
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("src_dtype", ["fp32", "bf16"])
+def test_attention_tiny(dev, mode, src_dtype):
+    w = TINY
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    say(f"attention tiny mode={mode} inputs={src_dtype}")
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=0, dtype=torch.float32)
+    qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
+    scale = 1 / math.sqrt(w.d)
+    o, lse = run_attention(dev, geom, mask, qb, kb, vb, w.kinds, w.bq, w.bkv, mode, want_lse=True)
+    for h, kind in enumerate(w.kinds):
+        src = (q, k, v) if src_dtype == "fp32" else (qb, kb, vb)
+        ref, ref_lse = oracle_head(geom, mask, src[0][0, h], src[1][0, h], src[2][0, h], kind, mode, w.bq, w.bkv,
+                                   scale)
+        assert_close(o[0, h].float().numpy(), ref, f"head {h}")
+        if src_dtype == "bf16":
+            assert np.abs(lse[0, h].numpy() - ref_lse).max() < 1e-3
+
+
+@pytest.mark.parametrize("tiles", [(128, 128), (256, 128), (64, 64), (128, 64), (32, 32), (512, 128), (256, 256)])
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_attention_small(dev, tiles, mode):
+    w = SMALL
+    bq, bkv = tiles
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    say(f"attention small tiles={tiles} mode={mode}")
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=1)
+    scale = 1 / math.sqrt(w.d)
+    o, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode)
+    rows = np.sort(np.random.default_rng(0).choice(w.N, 384, replace=False))
+    rows = np.unique(np.concatenate([rows, np.arange(128), np.arange(w.N - 128, w.N)]))
+    for h, kind in enumerate(w.kinds):
+        ref, _ = oracle_head(geom, mask, q[0, h], k[0, h], v[0, h], kind, mode, bq, bkv, scale, rows=rows)
+        assert_close(o[0, h, rows].float().numpy(), ref, f"head {h}")
+
+
+def test_gather_equals_permute_path_bitwise(dev):
+    """In-kernel gather of temporal rows gives the same bits as permute -> attention -> unpermute."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    for lay in (0, 1):
+        mask = (w.sink_frames, w.spatial_band, w.temporal_band, lay)
+        q, k, v = normal_qkv(2, w.heads, w.N, w.d, seed=2)
+        for bq, bkv, mode in ((128, 128, 2), (256, 128, 3), (64, 64, 1)):
+            say(f"gather layout={lay} tiles={bq}x{bkv} mode={mode}")
+            a, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=False)
+            b, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=True)
+            assert np.array_equal(i16(a), i16(b))
+
+
+def test_naive_and_exact_agree(dev):
+    """B1 and B2 keep the same pairs. B2 visits full tiles before boundary tiles, B1 in plain key
+    order, so the two agree to rounding; where a head has no boundary tile the visiting order is
+    the same and they agree bit for bit."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=3)
+    for bq, bkv in ((128, 128), (256, 128)):
+        say(f"naive vs exact tiles={bq}x{bkv}")
+        a, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, B.MAP_NAIVE)
+        b, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, B.MAP_EXACT)
+        ex = B.tilemap_views(B.svga_build_tilemap_host(geom, mask, bq, bkv, B.MAP_EXACT), geom, bq, bkv)
+        for h, kind in enumerate(w.kinds):
+            diff = np.abs(a[0, h].float().numpy() - b[0, h].float().numpy())
+            assert diff.max() < 4e-3
+            if ex["n_bnd"][kind].sum() == 0:
+                assert np.array_equal(i16(a[0, h]), i16(b[0, h]))
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_census_counts_every_kept_key(dev, mode):
+    """Q = 0: uniform weights over each row's kept keys; V[k, c] = [k mod d == c]; the output is the
+    exact share of kept keys per residue class. A missing or extra tile moves a column by far more
+    than bf16 rounding."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    say(f"census small mode={mode}")
+    q, k, v = census_qkv(1, w.heads, w.N, w.d)
+    o, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, w.bq, w.bkv, mode)
+    rows = np.arange(w.N)
+    for h, kind in enumerate(w.kinds):
+        ref, _ = oracle_head(geom, mask, q[0, h], k[0, h], v[0, h], kind, mode, w.bq, w.bkv, 0.1, rows=rows)
+        got = o[0, h].float().numpy()
+        rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)
+        say(f"  head {h}: max rel {rel[ref > 0].max():.3e}")
+        assert (got[ref == 0] == 0).all()
+        assert rel[ref > 0].max() < 2 ** -7
+
+
+@pytest.mark.parametrize("geom,mask,tiles,kinds", [
+    ((3, 5, 7), (1, 1, 3, 0), (64, 64), (0, 1)),         # ragged: 105 tokens, tiles past the end
+    ((3, 5, 7), (0, 0, 0, 0), (32, 32), (0, 1)),         # no sink, zero bands: each row keeps its own frame/position
+    ((2, 3, 3), (1, 5, 20, 0), (128, 128), (1, 0)),      # one tile larger than the sequence
+    ((6, 4, 4), (2, 1, 3, 1), (64, 32), (1, 1, 0)),      # literal order with two sink frames
+    ((5, 7, 3), (5, 0, 1, 0), (32, 64), (1, 0)),         # every frame a sink frame
+])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_attention_edge_cases(dev, geom, mask, tiles, kinds, mode):
+    F, H, W = geom
+    N = F * H * W
+    bq, bkv = tiles
+    say(f"edge geom={geom} mask={mask} tiles={tiles} kinds={kinds} mode={mode}")
+    q, k, v = normal_qkv(2, len(kinds), N, 128, seed=5)
+    q = q * 3
+    for gather in (False, True):
+        o, lse = run_attention(dev, geom, mask, q, k, v, kinds, bq, bkv, mode, gather=gather, want_lse=not gather)
+        for b in range(2):
+            for h, kind in enumerate(kinds):
+                ref, ref_lse = oracle_head(geom, mask, q[b, h], k[b, h], v[b, h], kind, mode, bq, bkv,
+                                           1 / math.sqrt(128))
+                assert_close(o[b, h].float().numpy(), ref, f"b{b} h{h} gather={gather}")
+                if lse is not None:
+                    fin = np.isfinite(ref_lse)
+                    assert np.array_equal(np.isfinite(lse[b, h].numpy()), fin)
+                    if fin.any():
+                        assert np.abs(lse[b, h].numpy()[fin] - ref_lse[fin]).max() < 1e-3
+
+
+# ---------------------------------------------------------------- routing
+
+def check_routing(dev, geom, mask, q, k, v, idx, tol=1e-3):
+    F, H, W = geom
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    flags, err = B.svga_route_heads(qd, kd, vd, geom, mask, torch.as_tensor(idx, dtype=torch.int32).to(dev))
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(q.shape[-1])
+    f_ref, e_ref = O.route_heads(q.double().numpy(), k.double().numpy(), v.double().numpy(), F, H, W, mask[0],
+                                 mask[1], mask[2], np.asarray(idx), scale)
+    e = err.cpu().numpy()
+    f = flags.cpu().numpy()
+    say(f"  err gpu {e.reshape(-1, 2)[:4].tolist()} oracle {e_ref.reshape(-1, 2)[:4].tolist()}")
+    big = np.maximum(e_ref.max(axis=-1, keepdims=True), 1e-30)
+    assert (np.abs(e - e_ref) <= tol * big).all()
+    decided = np.abs(e_ref[..., 1] - e_ref[..., 0]) > tol * big[..., 0]
+    assert np.array_equal(f[decided], f_ref[decided])
+    return f, f_ref
+
+
+@pytest.mark.parametrize("n", [1, 7, 32, 33, 64])
+def test_routing_tiny(dev, n):
+    w = TINY
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    say(f"routing tiny n_samples={n}")
+    q, k, v = normal_qkv(2, 3, w.N, w.d, seed=4)
+    idx = sample_indices(w.N, n, seed=n).numpy()
+    check_routing(dev, geom, mask, q * 2, k, v, idx)
+
+
+def test_routing_finds_planted_kinds(dev):
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    kinds = (0, 1, 1, 0, 1, 0)
+    say("routing planted small")
+    q, k, v = planted_qkv(1, w.F, w.H, w.W, w.d, kinds, seed=7)
+    idx = sample_indices(w.N, 64, seed=0).numpy()
+    f, f_ref = check_routing(dev, geom, mask, q, k, v, idx)
+    assert tuple(f[0]) == kinds and tuple(f_ref[0]) == kinds
+
+
+def test_routing_head_dim_128_ragged_chunks(dev):
+    geom = (5, 7, 9)          # 315 tokens: chunks end mid-tile
+    mask = (1, 1, 4, 0)
+    say("routing d128 ragged")
+    q, k, v = normal_qkv(1, 2, 315, 128, seed=6)
+    idx = sample_indices(315, 40, seed=1).numpy()
+    check_routing(dev, geom, mask, q * 3, k, v, idx)

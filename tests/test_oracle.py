@@ -186,6 +186,14 @@ def test_tile_counts_match_interval_count(F, H, W, kind, layout, tiles, sink):
     assert np.array_equal(c, _interval_counts(F, H, W, kind, sink, band, layout, bq, bkv))
 
 
+def test_tile_counts_subset_equals_full_scan():
+    """Restricting the scan to some query tiles leaves those rows unchanged."""
+    full = O.tile_counts(5, 3, 7, 1, 1, 1, 2, 0, 16, 8)
+    part = O.tile_counts(5, 3, 7, 1, 1, 1, 2, 0, 16, 8, q_tiles=[0, 3, 3, 6])
+    assert np.array_equal(part[[0, 3, 6]], full[[0, 3, 6]])
+    assert (np.delete(part, [0, 3, 6], axis=0) == -1).all()
+
+
 def test_tiny_spatial_classes_match_hand_grid():
     """Pin: hand-derived class grid (tests/golden/tiny_spatial_classes.txt)."""
     want = np.array([[O.FULL if x == "F" else O.SKIP for x in row] for row in _read("tiny_spatial_classes.txt")])
