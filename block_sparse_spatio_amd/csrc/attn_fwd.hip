@@ -10,7 +10,10 @@
 //
 // Design (one workgroup per (batch*head, query tile)):
 // * WAVES waves, each owning QB blocks of 32 query rows. Q stays in VGPRs as
-//   the B operand of v_mfma_f32_32x32x16_bf16 for the whole kernel.
+//   the B operand of v_mfma_f32_32x32x16_bf16 for the whole kernel. With
+//   QB = 1 and 8 waves a workgroup holds two waves per SIMD and each wave
+//   stays within 256 registers, so one wave's softmax (VALU) runs while the
+//   other wave's matrix products occupy the MFMA pipe.
 // * Scores are computed transposed, S^T = K Q^T (A = K rows from LDS), so each
 //   lane holds one query's scores: row max and row sum are lane-local plus one
 //   exchange with the other 32-lane half.
@@ -18,14 +21,18 @@
 //   the 32x32 accumulator layout (register i of lane l is row 8(i/4)+4(l/32)+i%4)
 //   this puts keys 16m+8h..16m+8h+7 in registers 8m..8m+7 of half h, which is
 //   exactly the B-operand layout that P^T needs for O^T = V^T P^T.
-// * K and V sub-tiles of KSUB keys are staged through LDS, double-buffered,
-//   with the global loads for step s+2 in flight while step s computes. V is
-//   transposed into LDS (d-major) while staging so the V^T operand is a plain
-//   16-byte LDS read. LDS chunks are XOR-swizzled against bank conflicts.
-// * The FULL list runs without any predicate; on BOUNDARY tiles the exact
-//   mask (NAIVE/EXACT maps) or the padding mask (DENSE/ROUNDED maps) sets
-//   excluded scores to -inf. A row with no kept key so far keeps a zero
-//   exponent base, so no NaN appears.
+// * K and V sub-tiles of KSUB keys are copied to LDS, double-buffered, with
+//   the global loads for step s+2 in flight while step s computes; V^T
+//   operands come from transposing LDS reads; rows are padded so that all
+//   operand reads are conflict-free (tile_stage.h).
+// * Lazy rescaling: a row keeps its exponent base until its running max
+//   exceeds the base by more than 2^8 in probability scale; only then are the
+//   output accumulator and the row sum rescaled. The final normalisation uses
+//   the same base, so the result is the plain softmax.
+// * The FULL list runs the unmasked body; BOUNDARY tiles run a separate
+//   instantiation that applies the exact mask (NAIVE / EXACT maps) or the
+//   padding mask (DENSE / ROUNDED maps). A row with no kept key so far keeps
+//   an exponent base of zero, so no NaN appears.
 // * Workgroups are remapped so that consecutive query tiles of one head run
 //   on the same XCD (dispatch is round-robin over the 8 XCDs), sharing K/V
 //   in that XCD's L2.
@@ -48,19 +55,125 @@ struct KArgs {
     Geo g;
     int32_t tq, tk, bkv;
     int32_t exact;          // 1: exact mask on boundary tiles, 0: padding only
-    int32_t gather;         // 1: temporal heads read/write frame-major rows through the permutation
     int32_t total, per_xcd;
     float c2;               // softmax_scale * log2(e)
     float scale;
 };
 
-template <int D, int QB, int WAVES, int KSUB>
-__global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
+constexpr float kRescaleLog2 = 8.0f;   // rescale when the running max grows by more than 2^8
+
+template <int D, int QB>
+struct WaveState {
+    static constexpr int DB = D / 32;
+    f32x16 oacc[QB][DB];
+    float base[QB];   // exponent base of the row (log2 domain, scale folded in)
+    float lsum[QB];   // per-lane partial row sum (this half's keys)
+};
+
+// One sub-tile of KSUB keys for one wave: S^T = K Q^T, mask (MASKED only),
+// online softmax with lazy rescaling, O^T += V^T P^T.
+template <int D, int QB, int KSUB, int NT, bool MASKED>
+__device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[QB][D / 16], WaveState<D, QB>& ws,
+                                         const RowKeys (&rk)[QB], const KArgs& a, int kb0, int lane) {
+    using St = Stager<D, KSUB, NT>;
+    constexpr int KBLK = KSUB / 32;
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int vlo = St::v_lane_off(lane);
+
+    f32x16 sacc[QB][KBLK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) sacc[qb][b] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) {
+            const bf16x8 ak = St::a_k(stg, b, c, l32, h);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                sacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[qb][c], sacc[qb][b], 0, 0, 0);
+        }
+    }
+
+    if constexpr (MASKED) {
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = kb0 + acc_key(b, i, h);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < a.g.N);
+                    if (!keep) sacc[qb][b][i] = -INFINITY;
+                }
+            }
+        }
+    }
+
+    bf16x8 preg[QB][KSUB / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float mx = sacc[qb][0][0];
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b)
+#pragma unroll
+            for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[qb][b][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // a new base is needed when this tile's max exceeds the current base by more than 2^8
+        const float cand = mx * a.c2;
+        const bool grow = cand > ws.base[qb] + kRescaleLog2;
+        if (__any(grow)) {
+            const float nb = grow ? cand : ws.base[qb];
+            // rows that keep their base scale by 1 (their base may still be -inf);
+            // a growing row whose old base is -inf scales its zero state by 0
+            const float alpha = grow ? __builtin_amdgcn_exp2f(ws.base[qb] - nb) : 1.0f;
+            ws.base[qb] = nb;
+            ws.lsum[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) ws.oacc[qb][db] *= alpha;
+        }
+        const float nbase = ws.base[qb] == -INFINITY ? 0.f : -ws.base[qb];
+        float ls = 0.f;
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, nbase));
+                sacc[qb][b][i] = p;
+                ls += p;
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                bf16x8 pk;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sacc[qb][b][8 * m + e];
+                preg[qb][2 * b + m] = pk;
+            }
+        }
+        ws.lsum[qb] += ls;
+    }
+
+#pragma unroll
+    for (int m16 = 0; m16 < KSUB / 16; ++m16) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const bf16x8 av = St::a_v(stg, db, m16, vlo);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                ws.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, preg[qb][m16], ws.oacc[qb][db], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, int QB, int WAVES, int KSUB, bool GATHER>
+__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KArgs a) {
     constexpr int NT = WAVES * 64;
     constexpr int BQ = WAVES * QB * 32;
-    constexpr int KBLK = KSUB / 32;          // 32-key blocks per sub-tile
-    constexpr int DB = D / 32;               // 32-wide output d blocks
-    constexpr int DC = D / 16;               // 16-wide contraction chunks of Q.K
+    constexpr int DC = D / 16;
+    constexpr int DB = D / 32;
     using St = Stager<D, KSUB, NT>;
     __shared__ __attribute__((aligned(16))) char smem[2 * St::STAGE];
 
@@ -71,7 +184,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
     const int qt = logical - bh * a.tq;
     const int N = a.g.N;
     const int kind = a.flags[bh] ? SVGA_KIND_TEMPORAL : SVGA_KIND_SPATIAL;
-    const bool gat = a.gather && kind == SVGA_KIND_TEMPORAL;
+    const bool gat = GATHER && kind == SVGA_KIND_TEMPORAL;
     const int32_t* kvl = a.kv + ((size_t)kind * a.tq + qt) * a.tk;
     // list lengths and key-tile ids come from device memory: clamp them so
     // that no map content can send a load outside the K / V tensors
@@ -85,6 +198,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
     const uint16_t* qh = a.q + head_off;
     const uint16_t* kh = a.k + head_off;
     const uint16_t* vh = a.v + head_off;
+    const Geo& g = a.g;
 
     // ---- Q rows of this lane, as B operands (d = 16c + 8h .. +7)
     bf16x8 qreg[QB][DC];
@@ -93,7 +207,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const int row = qt * BQ + (wave * QB + qb) * 32 + l32;
         if (row < N) {
-            const int qsrc = gat ? temporal_src(a.g, row) : row;
+            const int qsrc = gat ? temporal_src(g, row) : row;
             const bf16x8* p = reinterpret_cast<const bf16x8*>(qh + (size_t)qsrc * D + 8 * h);
 #pragma unroll
             for (int c = 0; c < DC; ++c) qreg[qb][c] = p[2 * c];
@@ -101,24 +215,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
 #pragma unroll
             for (int c = 0; c < DC; ++c) qreg[qb][c] = bf16x8{};
         }
-        rk[qb] = row_keys(a.g, kind, row < N ? row : N - 1);
+        rk[qb] = row_keys(g, kind, row < N ? row : N - 1);
     }
 
-    f32x16 oacc[QB][DB];
-    float mrow[QB], lrow[QB];
+    WaveState<D, QB> ws;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        mrow[qb] = -INFINITY;
-        lrow[qb] = 0.f;
+        ws.base[qb] = -INFINITY;
+        ws.lsum[qb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+        for (int db = 0; db < DB; ++db) ws.oacc[qb][db] = f32x16{};
     }
 
     const int nsub = a.bkv / KSUB;
     const int steps = ntiles * nsub;
     St st;
-    const Geo& g = a.g;
-    auto src = [&](int j) { return gat ? temporal_src(g, j) : j; };
+    auto src = [&](int j) { return GATHER ? (gat ? temporal_src(g, j) : j) : j; };
     auto key_base = [&](int s) {
         const int t = s / nsub;
         return imin(imax(kvl[t], 0), a.tk - 1) * a.bkv + (s - t * nsub) * KSUB;
@@ -134,89 +246,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
     for (int s = 0; s < steps; ++s) {
         const char* stg = smem + (s & 1) * St::STAGE;
         const int kb0 = key_base(s);
-        const bool boundary = (s / nsub) >= nf;
-
-        // ---- S^T = K Q^T
-        f32x16 sacc[QB][KBLK];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b) sacc[qb][b] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b) {
-                const bf16x8 ak = St::a_k(stg, b, c, l32, h);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[qb][c], sacc[qb][b], 0, 0, 0);
-            }
-        }
-
-        // ---- mask (boundary tiles only)
-        if (boundary) {
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = kb0 + acc_key(b, i, h);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < N);
-                        if (!keep) sacc[qb][b][i] = -INFINITY;
-                    }
-                }
-            }
-        }
-
-        // ---- online softmax (base-2 exponent, scale folded in)
-        bf16x8 preg[QB][KSUB / 16];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[qb][b][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrow[qb], mx);
-            const float base = mnew == -INFINITY ? 0.f : mnew * a.c2;
-            const float alpha = __builtin_amdgcn_exp2f(mrow[qb] * a.c2 - base);
-            mrow[qb] = mnew;
-            float ls = 0.f;
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, -base));
-                    sacc[qb][b][i] = p;
-                    ls += p;
-                }
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    bf16x8 pk;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sacc[qb][b][8 * m + e];
-                    preg[qb][2 * b + m] = pk;
-                }
-            }
-            lrow[qb] = lrow[qb] * alpha + ls;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-        }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int m16 = 0; m16 < KSUB / 16; ++m16) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 av = St::a_v(stg, db, m16, l32, h);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, preg[qb][m16], oacc[qb][db], 0, 0, 0);
-            }
-        }
-
+        if ((s / nsub) < nf) sub_tile<D, QB, KSUB, NT, false>(stg, qreg, ws, rk, a, kb0, lane);
+        else sub_tile<D, QB, KSUB, NT, true>(stg, qreg, ws, rk, a, kb0, lane);
         if (s + 1 < steps) {
             st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
             if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
@@ -224,24 +255,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = m*scale + ln l
+    // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = (base + log2 l) * ln 2
     uint16_t* oh = a.o + head_off;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float lt = lrow[qb] + __shfl_xor(lrow[qb], 32);
+        const float lt = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const int row = qt * BQ + (wave * QB + qb) * 32 + l32;
         if (row < N) {
-            const int orow = gat ? temporal_src(a.g, row) : row;
+            const int orow = gat ? temporal_src(g, row) : row;
             uint16_t* op = oh + (size_t)orow * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    __bf16 b0 = (__bf16)(oacc[qb][db][4 * gq + 0] * inv);
-                    __bf16 b1 = (__bf16)(oacc[qb][db][4 * gq + 1] * inv);
-                    __bf16 b2 = (__bf16)(oacc[qb][db][4 * gq + 2] * inv);
-                    __bf16 b3 = (__bf16)(oacc[qb][db][4 * gq + 3] * inv);
+                    __bf16 b0 = (__bf16)(ws.oacc[qb][db][4 * gq + 0] * inv);
+                    __bf16 b1 = (__bf16)(ws.oacc[qb][db][4 * gq + 1] * inv);
+                    __bf16 b2 = (__bf16)(ws.oacc[qb][db][4 * gq + 2] * inv);
+                    __bf16 b3 = (__bf16)(ws.oacc[qb][db][4 * gq + 3] * inv);
                     uint2 w;
                     w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
                     w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
@@ -249,29 +280,39 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_fwd_kernel(KArgs a) {
                 }
             }
             if (a.lse && h == 0)
-                a.lse[(size_t)bh * N + orow] = lt > 0.f ? mrow[qb] * a.scale + logf(lt) : -INFINITY;
+                a.lse[(size_t)bh * N + orow] =
+                    lt > 0.f ? (ws.base[qb] + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
         }
     }
 }
 
 template <int D, int QB, int WAVES, int KSUB>
-hipError_t launch_one(const KArgs& k, hipStream_t stream) {
+hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
     dim3 grid((unsigned)(k.per_xcd * 8));
-    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB>), grid, dim3(WAVES * 64), 0, stream, k);
+    if (gather)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, true>), grid, dim3(WAVES * 64), 0, stream, k);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, false>), grid, dim3(WAVES * 64), 0, stream, k);
     return hipGetLastError();
 }
 
-// bq -> (QB, WAVES): 32 -> (1,1), 64 -> (2,1), 128 -> (2,2), 256 -> (2,4), 512 -> (2,8).
-// KSUB = 64 when the workgroup has at least 128 threads and bkv is a multiple of 64, else 32.
+// bq -> (QB, WAVES): 32 -> (1,1), 64 -> (1,2), 128 -> (1,4), 256 -> (1,8), 512 -> (2,8).
+// KSUB = 64 when bkv is a multiple of 64, else 32.
 template <int D>
-hipError_t dispatch(const KArgs& k, int bq, int ksub, hipStream_t stream, bool* sup) {
+hipError_t dispatch(const KArgs& k, int bq, int ksub, bool gather, hipStream_t stream, bool* sup) {
     *sup = true;
-    if (bq == 32) return launch_one<D, 1, 1, 32>(k, stream);
-    if (bq == 64) return launch_one<D, 2, 1, 32>(k, stream);
-    if (bq == 128) return ksub == 64 ? launch_one<D, 2, 2, 64>(k, stream) : launch_one<D, 2, 2, 32>(k, stream);
-    if (bq == 256) return ksub == 64 ? launch_one<D, 2, 4, 64>(k, stream) : launch_one<D, 2, 4, 32>(k, stream);
-    if constexpr (D == 128) {
-        if (bq == 512) return ksub == 64 ? launch_one<D, 2, 8, 64>(k, stream) : launch_one<D, 2, 8, 32>(k, stream);
+    if (ksub == 64) {
+        if (bq == 32) return launch_one<D, 1, 1, 64>(k, gather, stream);
+        if (bq == 64) return launch_one<D, 1, 2, 64>(k, gather, stream);
+        if (bq == 128) return launch_one<D, 1, 4, 64>(k, gather, stream);
+        if (bq == 256) return launch_one<D, 1, 8, 64>(k, gather, stream);
+        if (bq == 512) return launch_one<D, 2, 8, 64>(k, gather, stream);
+    } else {
+        if (bq == 32) return launch_one<D, 1, 1, 32>(k, gather, stream);
+        if (bq == 64) return launch_one<D, 1, 2, 32>(k, gather, stream);
+        if (bq == 128) return launch_one<D, 1, 4, 32>(k, gather, stream);
+        if (bq == 256) return launch_one<D, 1, 8, 32>(k, gather, stream);
+        if (bq == 512) return launch_one<D, 2, 8, 32>(k, gather, stream);
     }
     *sup = false;
     return hipSuccess;
@@ -281,7 +322,7 @@ hipError_t dispatch(const KArgs& k, int bq, int ksub, hipStream_t stream, bool* 
 
 bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv) {
     if (head_dim != 64 && head_dim != 128) return false;
-    if (!(bq == 32 || bq == 64 || bq == 128 || bq == 256 || (bq == 512 && head_dim == 128))) return false;
+    if (!(bq == 32 || bq == 64 || bq == 128 || bq == 256 || bq == 512)) return false;
     return bkv >= 32 && bkv <= 512 && bkv % 32 == 0;
 }
 
@@ -303,15 +344,13 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* suppor
     k.tk = a.L.tk;
     k.bkv = a.bkv;
     k.exact = (a.mode == SVGA_MAP_NAIVE || a.mode == SVGA_MAP_EXACT) ? 1 : 0;
-    k.gather = a.gather;
     k.total = a.BH * a.L.tq;
     k.per_xcd = (k.total + 7) / 8;
     k.c2 = a.scale * 1.4426950408889634f;
     k.scale = a.scale;
-    const int threads = a.bq <= 64 ? 64 : a.bq;
-    const int ksub = (threads >= 256 && a.bkv % 64 == 0) ? 64 : 32;
-    if (a.head_dim == 64) return dispatch<64>(k, a.bq, ksub, stream, supported);
-    return dispatch<128>(k, a.bq, ksub, stream, supported);
+    const int ksub = a.bkv % 64 == 0 ? 64 : 32;
+    if (a.head_dim == 64) return dispatch<64>(k, a.bq, ksub, a.gather != 0, stream, supported);
+    return dispatch<128>(k, a.bq, ksub, a.gather != 0, stream, supported);
 }
 
 }  // namespace svga

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(QBLK * 3 * 64) void route_partial_kernel(RArgs a) {
             }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8 av = St::a_v(stg, db, m16, l32, h);
+                const bf16x8 av = St::a_v(stg, db, m16, St::v_lane_off(lane));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, hi8, oacc[db], 0, 0, 0);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lo8, oacc[db], 0, 0, 0);
             }
