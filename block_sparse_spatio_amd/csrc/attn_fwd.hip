@@ -29,8 +29,8 @@
 //   exceeds the base by more than 2^8 in probability scale; only then are the
 //   output accumulator and the row sum rescaled. The final normalisation uses
 //   the same base, so the result is the plain softmax.
-// * The FULL list runs the unmasked body; BOUNDARY tiles run a separate
-//   instantiation that applies the exact mask (NAIVE / EXACT maps) or the
+// * FULL tiles run a loop with no mask code at all; BOUNDARY tiles run a
+//   second loop that applies the exact mask (NAIVE / EXACT maps) or the
 //   padding mask (DENSE / ROUNDED maps). A row with no kept key so far keeps
 //   an exponent base of zero, so no NaN appears.
 // * Workgroups are remapped so that consecutive query tiles of one head run
@@ -61,6 +61,15 @@ struct KArgs {
 };
 
 constexpr float kRescaleLog2 = 8.0f;   // rescale when the running max grows by more than 2^8
+
+// max of x over the two 32-lane halves, in every lane: v_permlane32_swap
+// exchanges the halves of its two operands, so one of the two results holds
+// the other half's value whatever the lane.
+__device__ __forceinline__ float half_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(fmaxf(x, __builtin_bit_cast(float, (uint32_t)r[0])), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
 
 template <int D, int QB>
 struct WaveState {
@@ -121,7 +130,7 @@ __device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[Q
         for (int b = 0; b < KBLK; ++b)
 #pragma unroll
             for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[qb][b][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = half_max(mx);
         // a new base is needed when this tile's max exceeds the current base by more than 2^8
         const float cand = mx * a.c2;
         const bool grow = cand > ws.base[qb] + kRescaleLog2;
@@ -168,8 +177,11 @@ __device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[Q
     }
 }
 
+// QB = 1: at most 256 registers per wave, so two waves share each SIMD (two
+// 4-wave workgroups, or one 8-wave workgroup, per CU).
 template <int D, int QB, int WAVES, int KSUB, bool GATHER>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
+void attn_fwd_kernel(KArgs a) {
     constexpr int NT = WAVES * 64;
     constexpr int BQ = WAVES * QB * 32;
     constexpr int DC = D / 16;
@@ -243,16 +255,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(KArgs a) {
     }
     __syncthreads();
 
-    for (int s = 0; s < steps; ++s) {
-        const char* stg = smem + (s & 1) * St::STAGE;
-        const int kb0 = key_base(s);
-        if ((s / nsub) < nf) sub_tile<D, QB, KSUB, NT, false>(stg, qreg, ws, rk, a, kb0, lane);
-        else sub_tile<D, QB, KSUB, NT, true>(stg, qreg, ws, rk, a, kb0, lane);
+    // full tiles first (no mask code at all), then boundary tiles; both loops
+    // carry the same state and the same double-buffered K/V pipeline
+    auto advance = [&](int s) {
         if (s + 1 < steps) {
             st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
             if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
         }
         __syncthreads();
+    };
+    const int sfull = nf * nsub;
+    int s = 0;
+    for (; s < sfull; ++s) {
+        sub_tile<D, QB, KSUB, NT, false>(smem + (s & 1) * St::STAGE, qreg, ws, rk, a, key_base(s), lane);
+        advance(s);
+    }
+    for (; s < steps; ++s) {
+        sub_tile<D, QB, KSUB, NT, true>(smem + (s & 1) * St::STAGE, qreg, ws, rk, a, key_base(s), lane);
+        advance(s);
     }
 
     // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = (base + log2 l) * ln 2
