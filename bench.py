@@ -195,7 +195,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops_alg / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(args.mode, bq, bkv),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE, calibrated on a copy kernel)",
             "avg_ms": round(t_attn, 4),
             "algorithmic_flop": flop_alg,
             "executed_tile_tflops": round(tflops_exec, 2),
@@ -225,6 +226,25 @@ def main():
         "context_tpu_v6e_ms (pages, isolated kernel, other hardware)": PAGES_TPU_V6E_MS,
     }
     print(json.dumps(out), flush=True)
+
+
+def counted_traffic(mode, bq, bkv):
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE record, or None when the
+    record is for another configuration or the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "attn_fwd_headline_exact_256x128_hbm_counters.md")
+    try:
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", open(path).read(), re.S).group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    if (rec["mode"], rec["bq"], rec["bkv"]) != (mode, bq, bkv):
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
