@@ -71,6 +71,14 @@ __device__ __forceinline__ float half_max(float x) {
     return fmaxf(fmaxf(x, __builtin_bit_cast(float, (uint32_t)r[0])), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
+// Bits [a - kb0, b - kb0) of a 64-bit mask over keys kb0 .. kb0+63 (clamped).
+__device__ __forceinline__ uint64_t window_bits(int a, int b, int kb0) {
+    const int lo = imin(imax(a - kb0, 0), 64), hi = imin(imax(b - kb0, 0), 64);
+    const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
+    const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
+    return below_hi & ~below_lo;
+}
+
 template <int D, int QB>
 struct WaveState {
     static constexpr int DB = D / 32;
@@ -108,15 +116,42 @@ __device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[Q
     }
 
     if constexpr (MASKED) {
+        bool periodic = false;
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b) {
+        for (int qb = 0; qb < QB; ++qb) periodic = periodic || (a.exact && rk[qb].periodic);
+        if (__any(periodic)) {
+            // sink frames of the literal temporal order: an element-wise test
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = kb0 + acc_key(b, i, h);
+            for (int b = 0; b < KBLK; ++b) {
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < a.g.N);
-                    if (!keep) sacc[qb][b][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i) {
+                    const int j = kb0 + acc_key(b, i, h);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < a.g.N);
+                        if (!keep) sacc[qb][b][i] = -INFINITY;
+                    }
+                }
+            }
+        } else {
+            // the row keeps at most two key ranges: a 64-bit keep mask over the
+            // step's keys, shifted so that bit acc_key(b, i, 0) belongs to this
+            // lane's element (b, i); then a bit test and a select per element
+            // (a bitwise-select form of the same test is miscompiled by the
+            // gfx950 backend's three-input bit-op combine, so it is not used)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                uint64_t m = a.exact ? window_bits(rk[qb].a0, rk[qb].b0, kb0) | window_bits(rk[qb].a1, rk[qb].b1, kb0)
+                                     : window_bits(0, a.g.N, kb0);
+                m >>= acc_key(0, 0, h);   // 8 for the upper half-wave, 0 for the lower
+                const uint32_t mw[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
+#pragma unroll
+                for (int b = 0; b < KBLK; ++b) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int pos = acc_key(b, i, 0) - 32 * b;
+                        if (!((mw[b] >> pos) & 1u)) sacc[qb][b][i] = -INFINITY;
+                    }
                 }
             }
         }
