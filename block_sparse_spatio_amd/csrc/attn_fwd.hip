@@ -33,9 +33,11 @@
 //   second loop that applies the exact mask (NAIVE / EXACT maps) or the
 //   padding mask (DENSE / ROUNDED maps). A row with no kept key so far keeps
 //   an exponent base of zero, so no NaN appears.
-// * Workgroups are remapped so that consecutive query tiles of one head run
-//   on the same XCD (dispatch is round-robin over the 8 XCDs), sharing K/V
-//   in that XCD's L2.
+// * Workgroups keep the hardware's round-robin spread over the 8 XCDs:
+//   every XCD gets every eighth query tile of every head, so the XCDs carry
+//   equal work. (Grouping consecutive query tiles on one XCD for L2 reuse
+//   measured slower: the XCDs' shares of work then differ and the last XCD
+//   sets the end, while K/V re-reads are cheap at this arithmetic intensity.)
 #include "tile_stage.h"
 
 namespace svga {
@@ -55,7 +57,7 @@ struct KArgs {
     Geo g;
     int32_t tq, tk, bkv;
     int32_t exact;          // 1: exact mask on boundary tiles, 0: padding only
-    int32_t total, per_xcd;
+    int32_t total;
     float c2;               // softmax_scale * log2(e)
     float scale;
 };
@@ -225,7 +227,7 @@ void attn_fwd_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[2 * St::STAGE];
 
     const int id = blockIdx.x;
-    const int logical = (id & 7) * a.per_xcd + (id >> 3);
+    const int logical = id;
     if (logical >= a.total) return;
     const int bh = logical / a.tq;
     const int qt = logical - bh * a.tq;
@@ -343,7 +345,7 @@ void attn_fwd_kernel(KArgs a) {
 
 template <int D, int QB, int WAVES, int KSUB>
 hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
-    dim3 grid((unsigned)(k.per_xcd * 8));
+    dim3 grid((unsigned)k.total);
     if (gather)
         hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, true>), grid, dim3(WAVES * 64), 0, stream, k);
     else
@@ -400,7 +402,6 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* suppor
     k.bkv = a.bkv;
     k.exact = (a.mode == SVGA_MAP_NAIVE || a.mode == SVGA_MAP_EXACT) ? 1 : 0;
     k.total = a.BH * a.L.tq;
-    k.per_xcd = (k.total + 7) / 8;
     k.c2 = a.scale * 1.4426950408889634f;
     k.scale = a.scale;
     const int ksub = a.bkv % 64 == 0 ? 64 : 32;
