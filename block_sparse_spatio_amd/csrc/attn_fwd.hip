@@ -21,10 +21,18 @@
 //   the 32x32 accumulator layout (register i of lane l is row 8(i/4)+4(l/32)+i%4)
 //   this puts keys 16m+8h..16m+8h+7 in registers 8m..8m+7 of half h, which is
 //   exactly the B-operand layout that P^T needs for O^T = V^T P^T.
-// * K and V sub-tiles of KSUB keys are copied to LDS, double-buffered, with
+// * K and V sub-tiles of KSUB keys are copied to LDS through registers, with
 //   the global loads for step s+2 in flight while step s computes; V^T
 //   operands come from transposing LDS reads; rows are padded so that all
 //   operand reads are conflict-free (tile_stage.h).
+// * Ping-pong (8-wave workgroups): waves w and w+4 share a SIMD. Each step
+//   has two phases separated by workgroup barriers; in one phase a wave
+//   issues only matrix products (PV of the previous step, then Q K^T of this
+//   step), in the other only the softmax of this step's scores. Waves 0-3 run
+//   the phases in one order and waves 4-7 in the other, so on every SIMD one
+//   wave's products overlap the other wave's softmax. Smaller workgroups
+//   have no partner wave, and 64-row waves no registers to spare for the
+//   second phase's state: they run QK^T, softmax and PV in turn.
 // * Lazy rescaling: a row keeps its exponent base until its running max
 //   exceeds the base by more than 2^8 in probability scale; only then are the
 //   output accumulator and the row sum rescaled. The final normalisation uses
@@ -38,6 +46,8 @@
 //   equal work. (Grouping consecutive query tiles on one XCD for L2 reuse
 //   measured slower: the XCDs' shares of work then differ and the last XCD
 //   sets the end, while K/V re-reads are cheap at this arithmetic intensity.)
+#include <type_traits>
+
 #include "tile_stage.h"
 
 namespace svga {
@@ -89,129 +99,212 @@ struct WaveState {
     float lsum[QB];   // per-lane partial row sum (this half's keys)
 };
 
-// One sub-tile of KSUB keys for one wave: S^T = K Q^T, mask (MASKED only),
-// online softmax with lazy rescaling, O^T += V^T P^T.
-template <int D, int QB, int KSUB, int NT, bool MASKED>
-__device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[QB][D / 16], WaveState<D, QB>& ws,
-                                         const RowKeys (&rk)[QB], const KArgs& a, int kb0, int lane) {
+// The pieces of one step of KSUB keys for one wave.
+template <int D, int QB, int KSUB, int NT>
+struct Step {
     using St = Stager<D, KSUB, NT>;
-    constexpr int KBLK = KSUB / 32;
-    constexpr int DC = D / 16;
-    constexpr int DB = D / 32;
-    const int l32 = lane & 31, h = lane >> 5;
-    const int vlo = St::v_lane_off(lane);
+    static constexpr int KBLK = KSUB / 32;
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    typedef f32x16 Scores[QB][KBLK];
+    typedef bf16x8 Probs[QB][KSUB / 16];
 
-    f32x16 sacc[QB][KBLK];
+    // S^T = K Q^T for the keys staged at stg (compiler-scheduled).
+    static __device__ __forceinline__ void qk(const char* stg, const bf16x8 (&qreg)[QB][DC], Scores& sacc, int lane) {
+        const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b) sacc[qb][b] = f32x16{};
+            for (int b = 0; b < KBLK; ++b) sacc[qb][b] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
+        for (int c = 0; c < DC; ++c)
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b) {
-            const bf16x8 ak = St::a_k(stg, b, c, l32, h);
+            for (int b = 0; b < KBLK; ++b) {
+                const bf16x8 ak = St::a_k(stg, b, c, l32, h);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[qb][c], sacc[qb][b], 0, 0, 0);
+            }
+    }
+
+    // O^T += V^T P^T for the values staged at stg (compiler-scheduled).
+    static __device__ __forceinline__ void pv(const char* stg, const Probs& preg, WaveState<D, QB>& ws, int lane) {
+        const int vlo = St::v_lane_off(lane);
+#pragma unroll
+        for (int m16 = 0; m16 < KSUB / 16; ++m16)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 av = St::a_v(stg, db, m16, vlo);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    ws.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, preg[qb][m16], ws.oacc[qb][db], 0, 0, 0);
+            }
+    }
+
+    // Matrix phase of the ping-pong: PV of the previous step (DO_PV, values at
+    // vstg), then S^T = K Q^T of this step (DO_QK, keys at kstg). One product
+    // per slot, each slot's operand read issued LA slots ahead, the order
+    // fixed with sched_barrier so that the products issue back to back and
+    // the operand registers in flight stay bounded.
+    template <bool DO_PV, bool DO_QK>
+    static __device__ __forceinline__ void products(const char* vstg, const char* kstg, const Probs& preg,
+                                                    const bf16x8 (&qreg)[QB][DC], Scores& sacc,
+                                                    WaveState<D, QB>& ws, int lane) {
+        constexpr int NPV = DO_PV ? (KSUB / 16) * DB : 0;
+        constexpr int NS = NPV + (DO_QK ? KBLK * DC : 0);
+        constexpr int LA = 6;
+        const int l32 = lane & 31, h = lane >> 5;
+        const int vlo = St::v_lane_off(lane);
+        // slot j < NPV: PV product (m16 = j / DB, db = j % DB); slot NPV + i:
+        // score product (c = i / KBLK, b = i % KBLK)
+        auto operand = [&](int j) __attribute__((always_inline)) {
+            if (j < NPV) return St::a_v(vstg, j % DB, j / DB, vlo);
+            const int i = j - NPV;
+            return St::a_k(kstg, i % KBLK, i / KBLK, l32, h);
+        };
+        if constexpr (DO_QK) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                sacc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[qb][c], sacc[qb][b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < KBLK; ++b) sacc[qb][b] = f32x16{};
+        }
+        bf16x8 op[NS];
+#pragma unroll
+        for (int j = 0; j < LA && j < NS; ++j) op[j] = operand(j);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (j + LA < NS) op[j + LA] = operand(j + LA);
+            if (j < NPV) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    ws.oacc[qb][j % DB] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j], preg[qb][j / DB], ws.oacc[qb][j % DB], 0, 0, 0);
+            } else {
+                const int i = j - NPV;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb][i % KBLK] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j], qreg[qb][i / KBLK], sacc[qb][i % KBLK], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    if constexpr (MASKED) {
-        bool periodic = false;
+    // Mask (MASKED only), row max with lazy rescaling, P = exp2(S c2 - base)
+    // rounded to bf16 for the PV products, fp32 row sums.
+    template <bool MASKED>
+    static __device__ __forceinline__ void softmax(Scores& sacc, Probs& preg, WaveState<D, QB>& ws,
+                                                   const RowKeys (&rk)[QB], const KArgs& a, int kb0, int lane) {
+        const int h = lane >> 5;
+        if constexpr (MASKED) {
+            bool periodic = false;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) periodic = periodic || (a.exact && rk[qb].periodic);
-        if (__any(periodic)) {
-            // sink frames of the literal temporal order: an element-wise test
+            for (int qb = 0; qb < QB; ++qb) periodic = periodic || (a.exact && rk[qb].periodic);
+            if (__any(periodic)) {
+                // sink frames of the literal temporal order: an element-wise test
+#pragma unroll
+                for (int b = 0; b < KBLK; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = kb0 + acc_key(b, i, h);
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) {
+                            const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < a.g.N);
+                            if (!keep) sacc[qb][b][i] = -INFINITY;
+                        }
+                    }
+            } else {
+                // the row keeps at most two key ranges: a 64-bit keep mask over the
+                // step's keys, shifted so that bit acc_key(b, i, 0) belongs to this
+                // lane's element (b, i); then a bit test and a select per element
+                // (a bitwise-select form of the same test is miscompiled by the
+                // gfx950 backend's three-input bit-op combine, so it is not used)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    uint64_t m = a.exact ? window_bits(rk[qb].a0, rk[qb].b0, kb0) | window_bits(rk[qb].a1, rk[qb].b1, kb0)
+                                         : window_bits(0, a.g.N, kb0);
+                    m >>= acc_key(0, 0, h);   // 8 for the upper half-wave, 0 for the lower
+                    const uint32_t mw[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
+#pragma unroll
+                    for (int b = 0; b < KBLK; ++b)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int pos = acc_key(b, i, 0) - 32 * b;
+                            if (!((mw[b] >> pos) & 1u)) sacc[qb][b][i] = -INFINITY;
+                        }
+                }
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = sacc[qb][0][0];
+#pragma unroll
+            for (int b = 0; b < KBLK; ++b)
+#pragma unroll
+                for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[qb][b][i]);
+            mx = half_max(mx);
+            // a new base is needed when this step's max exceeds the current base by more than 2^8
+            const float cand = mx * a.c2;
+            const bool grow = cand > ws.base[qb] + kRescaleLog2;
+            if (__any(grow)) {
+                const float nb = grow ? cand : ws.base[qb];
+                // rows that keep their base scale by 1 (their base may still be -inf);
+                // a growing row whose old base is -inf scales its zero state by 0
+                const float alpha = grow ? __builtin_amdgcn_exp2f(ws.base[qb] - nb) : 1.0f;
+                ws.base[qb] = nb;
+                ws.lsum[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) ws.oacc[qb][db] *= alpha;
+            }
+            const float nbase = ws.base[qb] == -INFINITY ? 0.f : -ws.base[qb];
+            float ls = 0.f;
 #pragma unroll
             for (int b = 0; b < KBLK; ++b) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int j = kb0 + acc_key(b, i, h);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, nbase));
+                    sacc[qb][b][i] = p;
+                    ls += p;
+                }
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        const bool keep = a.exact ? row_keeps(a.g, rk[qb], j) : (j < a.g.N);
-                        if (!keep) sacc[qb][b][i] = -INFINITY;
-                    }
+                for (int m = 0; m < 2; ++m) {
+                    bf16x8 pk;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sacc[qb][b][8 * m + e];
+                    preg[qb][2 * b + m] = pk;
                 }
             }
-        } else {
-            // the row keeps at most two key ranges: a 64-bit keep mask over the
-            // step's keys, shifted so that bit acc_key(b, i, 0) belongs to this
-            // lane's element (b, i); then a bit test and a select per element
-            // (a bitwise-select form of the same test is miscompiled by the
-            // gfx950 backend's three-input bit-op combine, so it is not used)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                uint64_t m = a.exact ? window_bits(rk[qb].a0, rk[qb].b0, kb0) | window_bits(rk[qb].a1, rk[qb].b1, kb0)
-                                     : window_bits(0, a.g.N, kb0);
-                m >>= acc_key(0, 0, h);   // 8 for the upper half-wave, 0 for the lower
-                const uint32_t mw[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
-#pragma unroll
-                for (int b = 0; b < KBLK; ++b) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int pos = acc_key(b, i, 0) - 32 * b;
-                        if (!((mw[b] >> pos) & 1u)) sacc[qb][b][i] = -INFINITY;
-                    }
-                }
-            }
+            ws.lsum[qb] += ls;
         }
     }
 
-    bf16x8 preg[QB][KSUB / 16];
+    // The values a phase hands to the next one must be computed before the
+    // barrier between them: these empty asm statements use them there, so no
+    // instruction that produces them sinks into the following phase.
+    static __device__ __forceinline__ void fence(const Scores& sacc) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        float mx = sacc[qb][0][0];
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b)
+            for (int b = 0; b < KBLK; ++b)
 #pragma unroll
-            for (int i = (b == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, sacc[qb][b][i]);
-        mx = half_max(mx);
-        // a new base is needed when this tile's max exceeds the current base by more than 2^8
-        const float cand = mx * a.c2;
-        const bool grow = cand > ws.base[qb] + kRescaleLog2;
-        if (__any(grow)) {
-            const float nb = grow ? cand : ws.base[qb];
-            // rows that keep their base scale by 1 (their base may still be -inf);
-            // a growing row whose old base is -inf scales its zero state by 0
-            const float alpha = grow ? __builtin_amdgcn_exp2f(ws.base[qb] - nb) : 1.0f;
-            ws.base[qb] = nb;
-            ws.lsum[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) ws.oacc[qb][db] *= alpha;
-        }
-        const float nbase = ws.base[qb] == -INFINITY ? 0.f : -ws.base[qb];
-        float ls = 0.f;
-#pragma unroll
-        for (int b = 0; b < KBLK; ++b) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, nbase));
-                sacc[qb][b][i] = p;
-                ls += p;
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                bf16x8 pk;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sacc[qb][b][8 * m + e];
-                preg[qb][2 * b + m] = pk;
-            }
-        }
-        ws.lsum[qb] += ls;
+                for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(sacc[qb][b][i]));
     }
+    static __device__ __forceinline__ void fence(const Probs& preg, const WaveState<D, QB>& ws) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int m = 0; m < KSUB / 16; ++m) asm volatile("" ::"v"(preg[qb][m]));
+            asm volatile("" ::"v"(ws.lsum[qb]), "v"(ws.base[qb]));
+        }
+    }
+};
 
-#pragma unroll
-    for (int m16 = 0; m16 < KSUB / 16; ++m16) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const bf16x8 av = St::a_v(stg, db, m16, vlo);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                ws.oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, preg[qb][m16], ws.oacc[qb][db], 0, 0, 0);
-        }
-    }
+// Workgroup barrier between two phases: no data is handed over through LDS
+// here, and sched_barrier keeps the scheduler from moving work across it.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // QB = 1: at most 256 registers per wave, so two waves share each SIMD (two
@@ -219,12 +312,14 @@ __device__ __forceinline__ void sub_tile(const char* stg, const bf16x8 (&qreg)[Q
 template <int D, int QB, int WAVES, int KSUB, bool GATHER>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(KArgs a) {
+    constexpr bool PINGPONG = WAVES == 8 && QB == 1;
     constexpr int NT = WAVES * 64;
     constexpr int BQ = WAVES * QB * 32;
     constexpr int DC = D / 16;
     constexpr int DB = D / 32;
     using St = Stager<D, KSUB, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * St::STAGE];
+    using Sp = Step<D, QB, KSUB, NT>;
+    __shared__ __attribute__((aligned(16))) char smem[(PINGPONG ? 4 : 2) * St::STAGE];
 
     const int id = blockIdx.x;
     const int logical = id;
@@ -285,31 +380,133 @@ void attn_fwd_kernel(KArgs a) {
         return imin(imax(kvl[t], 0), a.tk - 1) * a.bkv + (s - t * nsub) * KSUB;
     };
 
-    if (steps > 0) {
-        st.load(kh, vh, key_base(0), N, src, tid);
-        st.store(smem, tid);
-        if (steps > 1) st.load(kh, vh, key_base(1), N, src, tid);
-    }
-    __syncthreads();
-
-    // full tiles first (no mask code at all), then boundary tiles; both loops
-    // carry the same state and the same double-buffered K/V pipeline
-    auto advance = [&](int s) {
-        if (s + 1 < steps) {
-            st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
-            if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
+    const int sfull = nf * nsub;
+    typename Sp::Scores sacc;
+    typename Sp::Probs preg;
+    if constexpr (!PINGPONG) {
+        if (steps > 0) {
+            st.load(kh, vh, key_base(0), N, src, tid);
+            st.store(smem, tid);
+            if (steps > 1) st.load(kh, vh, key_base(1), N, src, tid);
         }
         __syncthreads();
-    };
-    const int sfull = nf * nsub;
-    int s = 0;
-    for (; s < sfull; ++s) {
-        sub_tile<D, QB, KSUB, NT, false>(smem + (s & 1) * St::STAGE, qreg, ws, rk, a, key_base(s), lane);
-        advance(s);
-    }
-    for (; s < steps; ++s) {
-        sub_tile<D, QB, KSUB, NT, true>(smem + (s & 1) * St::STAGE, qreg, ws, rk, a, key_base(s), lane);
-        advance(s);
+        // full tiles first (no mask code at all), then boundary tiles; both
+        // loops carry the same state and the same double-buffered pipeline
+        auto advance = [&](int s) {
+            if (s + 1 < steps) {
+                st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
+                if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
+            }
+            __syncthreads();
+        };
+        int s = 0;
+        for (; s < sfull; ++s) {
+            const char* stg = smem + (s & 1) * St::STAGE;
+            Sp::qk(stg, qreg, sacc, lane);
+            Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane);
+            Sp::pv(stg, preg, ws, lane);
+            advance(s);
+        }
+        for (; s < steps; ++s) {
+            const char* stg = smem + (s & 1) * St::STAGE;
+            Sp::qk(stg, qreg, sacc, lane);
+            Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(s), lane);
+            Sp::pv(stg, preg, ws, lane);
+            advance(s);
+        }
+    } else {
+        // Ring of four stages filled through registers: at the top of step s
+        // the data of step s+1 (loaded one step earlier) goes to its stage,
+        // then the barrier, then the loads of step s+2 are issued. Step s's
+        // phases read stages s-1 (V) and s (K); four stages keep the store
+        // off those and off stage s-2, which the other group may still read
+        // until the barrier.
+        auto stage = [&](int s) { return (const char*)(smem + (s & 3) * St::STAGE); };
+        const bool lead = wave < WAVES / 2;   // products first
+        if (steps > 0) {
+            st.load(kh, vh, key_base(0), N, src, tid);
+            st.store(smem, tid);
+            if (steps > 1) st.load(kh, vh, key_base(1), N, src, tid);
+        }
+        auto top = [&](int s) __attribute__((always_inline)) {
+            if (s + 1 < steps) st.store(smem + ((s + 1) & 3) * St::STAGE, tid);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
+        };
+        auto soft = [&](auto masked, int t) __attribute__((always_inline)) {
+            if constexpr (decltype(masked)::value)
+                Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(t), lane);
+            else
+                Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane);
+            Sp::fence(preg, ws);
+        };
+        auto soft_rt = [&](int t) __attribute__((always_inline)) {
+            if (t < sfull) soft(std::false_type{}, t);
+            else soft(std::true_type{}, t);
+        };
+        // products of step s: PV of step s-1 (if any) and QK^T of step s (if any)
+        auto prod = [&](auto both, int s) __attribute__((always_inline)) {
+            if constexpr (decltype(both)::value)
+                Sp::template products<true, true>(stage(s - 1), stage(s), preg, qreg, sacc, ws, lane);
+            else if (s == 0)
+                Sp::template products<false, true>(nullptr, stage(0), preg, qreg, sacc, ws, lane);
+            else
+                Sp::template products<true, false>(stage(s - 1), nullptr, preg, qreg, sacc, ws, lane);
+            Sp::fence(sacc);
+        };
+        using Both = std::true_type;
+        using One = std::false_type;
+        // Every wave passes the same 2 * (steps + 1) barriers. The first and
+        // last steps are peeled so that the loops hold one form of each phase.
+        const int sf = imin(sfull, steps);
+        if (steps == 0) {
+            __syncthreads();
+            phase_barrier();
+        } else if (lead) {
+            top(0);
+            prod(One{}, 0);
+            phase_barrier();
+            soft_rt(0);
+            int s = 1;
+            for (; s < sf; ++s) {
+                top(s);
+                prod(Both{}, s);
+                phase_barrier();
+                soft(std::false_type{}, s);
+            }
+            for (; s < steps; ++s) {
+                top(s);
+                prod(Both{}, s);
+                phase_barrier();
+                soft(std::true_type{}, s);
+            }
+            top(steps);
+            prod(One{}, steps);
+            phase_barrier();
+        } else {
+            top(0);
+            phase_barrier();
+            prod(One{}, 0);
+            int s = 1;
+            for (; s < imin(sf + 1, steps); ++s) {
+                top(s);
+                soft(std::false_type{}, s - 1);
+                phase_barrier();
+                prod(Both{}, s);
+            }
+            for (; s < steps; ++s) {
+                top(s);
+                soft(std::true_type{}, s - 1);
+                phase_barrier();
+                prod(Both{}, s);
+            }
+            top(steps);
+            soft_rt(steps - 1);
+            phase_barrier();
+            prod(One{}, steps);
+        }
     }
 
     // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = (base + log2 l) * ln 2
