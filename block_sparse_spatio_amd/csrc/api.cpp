@@ -234,6 +234,12 @@ svga_status svga_sparse_attn_fwd(const void* d_q, const void* d_k, const void* d
     if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return fail(SVGA_EINVAL, "softmax_scale must be finite and > 0");
     if (!attn_supported(head_dim, bq, bkv))
         return fail(SVGA_EUNSUPPORTED, "no attention kernel for head_dim=%d bq=%d bkv=%d", head_dim, bq, bkv);
+    {
+        const int64_t head_bytes = (int64_t)geom->F * geom->H * geom->W * head_dim * 2;
+        if (head_bytes >= (int64_t(1) << 31))
+            return fail(SVGA_EUNSUPPORTED, "one head of K or V (N * head_dim * 2 = %lld bytes) must be below 2^31 bytes",
+                        (long long)head_bytes);
+    }
     Geo g = make_geo(*geom, *mask);
     MapLayout L = map_layout(g.N, bq, bkv);
     if (map_bytes < L.total) return fail(SVGA_ECAPACITY, "map_bytes %zu < required %zu", map_bytes, L.total);

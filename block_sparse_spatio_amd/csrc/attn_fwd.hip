@@ -30,7 +30,11 @@
 //   issues only matrix products (PV of the previous step, then Q K^T of this
 //   step), in the other only the softmax of this step's scores. Waves 0-3 run
 //   the phases in one order and waves 4-7 in the other, so on every SIMD one
-//   wave's products overlap the other wave's softmax. Smaller workgroups
+//   wave's products overlap the other wave's softmax. Only waves 4-7 move
+//   K and V: in their softmax phase they store the next step's staged
+//   registers and load the step after, one chunk between blocks of
+//   exponentials, so the step top is a bare barrier and the products of
+//   waves 0-3 never wait behind load issue. Smaller workgroups
 //   have no partner wave, and 64-row waves no registers to spare for the
 //   second phase's state: they run QK^T, softmax and PV in turn.
 // * Lazy rescaling: a row keeps its exponent base until its running max
@@ -191,10 +195,13 @@ struct Step {
     }
 
     // Mask (MASKED only), row max with lazy rescaling, P = exp2(S c2 - base)
-    // rounded to bf16 for the PV products, fp32 row sums.
-    template <bool MASKED>
+    // rounded to bf16 for the PV products, fp32 row sums. hook(k), k = 0 ..
+    // 2 KBLK - 1, is called after each block of 8 exponentials: code placed
+    // there (with its own sched_barriers) is spread over the phase.
+    template <bool MASKED, class Hook>
     static __device__ __forceinline__ void softmax(Scores& sacc, Probs& preg, WaveState<D, QB>& ws,
-                                                   const RowKeys (&rk)[QB], const KArgs& a, int kb0, int lane) {
+                                                   const RowKeys (&rk)[QB], const KArgs& a, int kb0, int lane,
+                                                   Hook hook) {
         const int h = lane >> 5;
         if constexpr (MASKED) {
             bool periodic = false;
@@ -261,17 +268,18 @@ struct Step {
 #pragma unroll
             for (int b = 0; b < KBLK; ++b) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, nbase));
-                    sacc[qb][b][i] = p;
-                    ls += p;
-                }
-#pragma unroll
                 for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                    for (int i = 8 * m; i < 8 * m + 8; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[qb][b][i], a.c2, nbase));
+                        sacc[qb][b][i] = p;
+                        ls += p;
+                    }
                     bf16x8 pk;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) pk[e] = (__bf16)sacc[qb][b][8 * m + e];
                     preg[qb][2 * b + m] = pk;
+                    if (qb == 0) hook(2 * b + m);
                 }
             }
             ws.lsum[qb] += ls;
@@ -329,7 +337,12 @@ void attn_fwd_kernel(KArgs a) {
     const int N = a.g.N;
     const int kind = a.flags[bh] ? SVGA_KIND_TEMPORAL : SVGA_KIND_SPATIAL;
     const bool gat = GATHER && kind == SVGA_KIND_TEMPORAL;
-    const int32_t* kvl = a.kv + ((size_t)kind * a.tq + qt) * a.tk;
+    // The tile list is read-only for the whole kernel; reading it through the
+    // constant address space lets the compiler use scalar loads for it even
+    // after barriers and LDS stores (a vector load there would put a full
+    // memory latency in front of every step's K / V loads).
+    typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+    const ConstI32 kvl = (ConstI32)(a.kv + ((size_t)kind * a.tq + qt) * a.tk);
     // list lengths and key-tile ids come from device memory: clamp them so
     // that no map content can send a load outside the K / V tensors
     const int nf = imin(imax(a.n_full[kind * a.tq + qt], 0), a.tk);
@@ -403,48 +416,70 @@ void attn_fwd_kernel(KArgs a) {
         for (; s < sfull; ++s) {
             const char* stg = smem + (s & 1) * St::STAGE;
             Sp::qk(stg, qreg, sacc, lane);
-            Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane);
+            Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane, [](int) {});
             Sp::pv(stg, preg, ws, lane);
             advance(s);
         }
         for (; s < steps; ++s) {
             const char* stg = smem + (s & 1) * St::STAGE;
             Sp::qk(stg, qreg, sacc, lane);
-            Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(s), lane);
+            Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(s), lane, [](int) {});
             Sp::pv(stg, preg, ws, lane);
             advance(s);
         }
     } else {
-        // Ring of four stages filled through registers: at the top of step s
-        // the data of step s+1 (loaded one step earlier) goes to its stage,
-        // then the barrier, then the loads of step s+2 are issued. Step s's
-        // phases read stages s-1 (V) and s (K); four stages keep the store
-        // off those and off stage s-2, which the other group may still read
-        // until the barrier.
+        // K / V staging: ring of four LDS stages, filled through the registers
+        // of waves 4-7 only. In its vector phase of step s each of those waves
+        // stores step s+1's registers to stage s+1 and loads step s+2's, one
+        // chunk at a time between the blocks of exponentials, so that neither
+        // the LDS writes nor the load issue form a burst; waves 0-3 issue no
+        // memory traffic in the loop. Step s's products read stages s-1 (V)
+        // and s (K); stage s+1 was last read in step s-2, so the four stages
+        // never overlap a write with a read, and the barrier at the top of step
+        // s+1 publishes stage s+1. Loads past the last step repeat its keys
+        // (never stored where anyone reads).
         auto stage = [&](int s) { return (const char*)(smem + (s & 3) * St::STAGE); };
+        auto wstage = [&](int s) { return smem + (s & 3) * St::STAGE; };
         const bool lead = wave < WAVES / 2;   // products first
-        if (steps > 0) {
-            st.load(kh, vh, key_base(0), N, src, tid);
-            st.store(smem, tid);
-            if (steps > 1) st.load(kh, vh, key_base(1), N, src, tid);
+        using Sh = Stager<D, KSUB, NT / 2>;
+        Sh sh;
+        const int htid = tid - NT / 2;
+        const __amdgpu_buffer_rsrc_t rsk = head_rsrc(kh, N * D * 2);
+        const __amdgpu_buffer_rsrc_t rsv = head_rsrc(vh, N * D * 2);
+        auto next_keys = [&](int s) __attribute__((always_inline)) { return key_base(imin(s + 2, steps - 1)); };
+        if (steps > 0 && !lead) {
+            sh.load(kh, vh, key_base(0), N, src, htid);
+            sh.store(wstage(0), htid);
+            sh.load(kh, vh, key_base(imin(1, steps - 1)), N, src, htid);
         }
-        auto top = [&](int s) __attribute__((always_inline)) {
-            if (s + 1 < steps) st.store(smem + ((s + 1) & 3) * St::STAGE, tid);
+        auto top = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            if (s + 2 < steps) st.load(kh, vh, key_base(s + 2), N, src, tid);
         };
-        auto soft = [&](auto masked, int t) __attribute__((always_inline)) {
+        // softmax of step t; with XFER (waves 4-7, step s) the stage transfer rides along
+        auto soft = [&](auto masked, auto xfer, int t, int s) __attribute__((always_inline)) {
+            char* dst = wstage(s + 1);
+            const int kb = decltype(xfer)::value ? next_keys(s) : 0;
+            // chunk r goes with hook point r * NH / CU (NH = KSUB / 16 points)
+            auto hook = [&](int k) __attribute__((always_inline)) {
+                if constexpr (decltype(xfer)::value) {
+                    constexpr int NH = KSUB / 16;
+#pragma unroll
+                    for (int r = 0; r < Sh::CU; ++r) {
+                        if (r * NH / Sh::CU != k) continue;
+                        __builtin_amdgcn_sched_barrier(0);
+                        sh.store_chunk(r, dst, htid);
+                        sh.load_chunk(r, rsk, rsv, kb, N, src, htid);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            };
             if constexpr (decltype(masked)::value)
-                Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(t), lane);
+                Sp::template softmax<true>(sacc, preg, ws, rk, a, key_base(t), lane, hook);
             else
-                Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane);
+                Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane, hook);
             Sp::fence(preg, ws);
-        };
-        auto soft_rt = [&](int t) __attribute__((always_inline)) {
-            if (t < sfull) soft(std::false_type{}, t);
-            else soft(std::true_type{}, t);
         };
         // products of step s: PV of step s-1 (if any) and QK^T of step s (if any)
         auto prod = [&](auto both, int s) __attribute__((always_inline)) {
@@ -458,6 +493,8 @@ void attn_fwd_kernel(KArgs a) {
         };
         using Both = std::true_type;
         using One = std::false_type;
+        using Yes = std::true_type;
+        using No = std::false_type;
         // Every wave passes the same 2 * (steps + 1) barriers. The first and
         // last steps are peeled so that the loops hold one form of each phase.
         const int sf = imin(sfull, steps);
@@ -465,45 +502,49 @@ void attn_fwd_kernel(KArgs a) {
             __syncthreads();
             phase_barrier();
         } else if (lead) {
-            top(0);
+            top();
             prod(One{}, 0);
             phase_barrier();
-            soft_rt(0);
+            if (0 < sfull) soft(No{}, No{}, 0, 0);
+            else soft(Yes{}, No{}, 0, 0);
             int s = 1;
             for (; s < sf; ++s) {
-                top(s);
+                top();
                 prod(Both{}, s);
                 phase_barrier();
-                soft(std::false_type{}, s);
+                soft(No{}, No{}, s, s);
             }
             for (; s < steps; ++s) {
-                top(s);
+                top();
                 prod(Both{}, s);
                 phase_barrier();
-                soft(std::true_type{}, s);
+                soft(Yes{}, No{}, s, s);
             }
-            top(steps);
+            top();
             prod(One{}, steps);
             phase_barrier();
         } else {
-            top(0);
+            top();
+            sh.store(wstage(1), htid);
+            sh.load(kh, vh, next_keys(0), N, src, htid);
             phase_barrier();
             prod(One{}, 0);
             int s = 1;
             for (; s < imin(sf + 1, steps); ++s) {
-                top(s);
-                soft(std::false_type{}, s - 1);
+                top();
+                soft(No{}, Yes{}, s - 1, s);
                 phase_barrier();
                 prod(Both{}, s);
             }
             for (; s < steps; ++s) {
-                top(s);
-                soft(std::true_type{}, s - 1);
+                top();
+                soft(Yes{}, Yes{}, s - 1, s);
                 phase_barrier();
                 prod(Both{}, s);
             }
-            top(steps);
-            soft_rt(steps - 1);
+            top();
+            if (steps - 1 < sfull) soft(No{}, No{}, steps - 1, steps);
+            else soft(Yes{}, No{}, steps - 1, steps);
             phase_barrier();
             prod(One{}, steps);
         }

@@ -33,6 +33,12 @@ __device__ __forceinline__ int pi32(int r) { return (r & ~12) | ((r & 4) << 1) |
 // Key index held by accumulator register i of a lane in half h of 32-key block b.
 __device__ __forceinline__ int acc_key(int b, int i, int h) { return b * 32 + pi32(8 * (i >> 2) + 4 * h + (i & 3)); }
 
+// Raw buffer resource over bytes bytes from p (no stride, gfx9 data format):
+// buffer loads at offsets at or past bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
 template <int D, int KSUB, int NT>
 struct Stager {
     static constexpr int RV = D / 8;                 // 16-byte chunks per row
@@ -69,6 +75,29 @@ struct Stager {
                 }
             }
         }
+    }
+
+    // Chunk r of load() alone, through buffer loads and without a branch: a
+    // row at or past limit gets an offset beyond the buffer's end, which the
+    // hardware reads as zero. rk / rv cover one head's K / V rows.
+    template <class Src>
+    __device__ __forceinline__ void load_chunk(int r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int kb0,
+                                               int limit, Src src, int tid) {
+        const int u = tid + r * NT;
+        const int row = u / RV, c = u % RV;
+        const int j = kb0 + row;
+        const int off = j < limit ? src(j) * (D * 2) + c * 16 : 0x7ffffff0;
+        kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+
+    // Chunk r of store() alone (CH a multiple of NT).
+    __device__ __forceinline__ void store_chunk(int r, char* stage, int tid) const {
+        static_assert(CH % NT == 0, "every thread owns CU chunks");
+        const int u = tid + r * NT;
+        const int row = u / RV, c = u % RV;
+        *reinterpret_cast<uint4*>(stage + k_off(row, c)) = kreg[r];
+        *reinterpret_cast<uint4*>(stage + v_off(row, c)) = vreg[r];
     }
 
     __device__ __forceinline__ void store(char* stage, int tid) const {

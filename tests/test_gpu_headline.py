@@ -99,6 +99,27 @@ def test_headline_sampled_rows(dev, headline, mode, bq):
         assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_headline_repeat_seeds(dev, seed):
+    """The EXACT 256 x 128 benchmark configuration on inputs drawn with two more seeds."""
+    w = HEADLINE
+    geom, mask = geom_mask(w)
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=seed)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say(f"headline attention seed={seed}")
+    o = pipeline(dev, w, q.to(dev), k.to(dev), v.to(dev), flags, 256, 128, B.MAP_EXACT).cpu()
+    scale = 1 / math.sqrt(w.d)
+    for h in (seed, 5 + seed):
+        rows = sample_rows(w.N, 256, 48, seed=40 + 10 * seed + h)
+        ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                                  w.kinds[h], w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, 256, 128, scale,
+                                  rows=rows)
+        err = np.abs(o[0, h, rows].double().numpy() - ref)
+        say(f"  head {h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+        assert np.isfinite(o[0, h, rows].float().numpy()).all()
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
 def test_headline_sharpened_scores(dev, headline):
     """Q scaled by 8: peaked softmax, O(1) outputs, so the absolute bound is tight."""
     w, q, k, v, qd, kd, vd = headline
