@@ -121,6 +121,16 @@ def main():
     t_perm = timed(lambda: B.svga_permute(kd, flags, geom, mask, out=kp), reps)
     t_unperm = timed(lambda: B.svga_unpermute(op, flags, geom, mask, out=o), reps)
     t_attn = timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op), reps)
+    # latency: median of 20 individually event-timed calls after 5 warm-ups
+    for _ in range(5):
+        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a_, b_ in ev:
+        a_.record()
+        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op)
+        b_.record()
+    torch.cuda.synchronize()
+    t_attn_median = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
 
     # work accounting from the tile map (read once, outside timing)
     host_map = B.tilemap_views(tmap.cpu().numpy(), geom, bq, bkv)
@@ -196,8 +206,10 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tflops_alg / PEAK_BF16_TFLOPS, 4),
             "traffic": counted_traffic(args.mode, bq, bkv),
+            "mfma_busy_pct": counted_mfma_busy(args.mode, bq, bkv),
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE, calibrated on a copy kernel)",
             "avg_ms": round(t_attn, 4),
+            "latency_median_ms": round(t_attn_median, 4),
             "algorithmic_flop": flop_alg,
             "executed_tile_tflops": round(tflops_exec, 2),
             "executed_tile_frac": round(tflops_exec / PEAK_BF16_TFLOPS, 4),
@@ -219,6 +231,7 @@ def main():
             "kept_pairs": kept_pairs,
             "kept_frac": round(kept_pairs / (w.heads * N * N), 5),
             "executed_tiles": n_exec,
+            "visited_frac": round(n_exec / (w.heads * off.tq * off.tk), 5),
             "boundary_of_executed": round(n_bnd / max(1, n_exec), 5),
             "routed_flags": routed,
         },
@@ -228,12 +241,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def counted_traffic(mode, bq, bkv):
-    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE record, or None when the
-    record is for another configuration or the kernel sources changed since the counters were taken."""
+def counter_record(name, key, mode, bq, bkv):
+    """A figure from a committed rocprofv3 counter summary under profiles/, or None when the record is for
+    another configuration or the kernel sources changed since the counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "attn_fwd_headline_exact_256x128_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", name)
     try:
         rec = json.loads(re.search(r"```json\n(.*?)\n```", open(path).read(), re.S).group(1))
     except (OSError, AttributeError, ValueError):
@@ -244,7 +257,17 @@ def counted_traffic(mode, bq, bkv):
     for f in rec["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+    return rec[key] if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def counted_traffic(mode, bq, bkv):
+    """HBM bytes per attention launch (calibrated FETCH_SIZE / WRITE_SIZE)."""
+    return counter_record("attn_fwd_headline_exact_256x128_hbm_counters.md", "traffic_bytes", mode, bq, bkv)
+
+
+def counted_mfma_busy(mode, bq, bkv):
+    """MFMA-busy % of the attention kernel (rocprofv3 MfmaUtil formula)."""
+    return counter_record("attn_fwd_headline_exact_256x128_mfma_counters.md", "mfma_busy_pct", mode, bq, bkv)
 
 
 def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
