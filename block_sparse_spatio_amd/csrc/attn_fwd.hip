@@ -87,14 +87,6 @@ __device__ __forceinline__ float half_max(float x) {
     return fmaxf(fmaxf(x, __builtin_bit_cast(float, (uint32_t)r[0])), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
-// Bits [a - kb0, b - kb0) of a 64-bit mask over keys kb0 .. kb0+63 (clamped).
-__device__ __forceinline__ uint64_t window_bits(int a, int b, int kb0) {
-    const int lo = imin(imax(a - kb0, 0), 64), hi = imin(imax(b - kb0, 0), 64);
-    const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
-    const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
-    return below_hi & ~below_lo;
-}
-
 template <int D, int QB>
 struct WaveState {
     static constexpr int DB = D / 32;

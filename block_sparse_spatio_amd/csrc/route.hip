@@ -11,14 +11,20 @@
 // Each wave holds 32 sampled queries as MFMA B operands and runs one of the
 // three softmaxes (dense, spatial mask, temporal mask) with its own running
 // max, sum and output; every K/V sub-tile of the chunk is staged through LDS
-// once and serves all waves. P is split into a bf16 high part and a bf16 remainder, both fed to
-// the MFMA, so the weighted sums keep about 16 mantissa bits. The partial
-// (max, sum, output) of every softmax is written to the workspace.
+// once and serves all waves. The softmax kind is wave-uniform, so each wave
+// runs a loop specialised to it; its mask is a 64-bit keep mask over the
+// step's keys (built from at most two key ranges, or from the frames the step
+// touches) and costs a bit test per score. P is split into a bf16 high part
+// and a bf16 remainder, both fed to the MFMA, so the weighted sums keep about
+// 16 mantissa bits. The partial (max, sum, output) of every softmax is
+// written to the workspace.
 // Pass 2 (route_merge_kernel): one workgroup per (sample, batch*head) merges
 // the chunk partials and forms that sample's ||o_x - o_dense||^2.
 // Pass 3 (route_flag_kernel): err_x = sum over samples, in sample order; the
 // flag is 1 (temporal) iff err_temporal < err_spatial.
 // Memory traffic: K and V read once; roofline is HBM bandwidth.
+#include <type_traits>
+
 #include "tile_stage.h"
 
 namespace svga {
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(QBLK * 3 * 64) void route_partial_kernel(RArgs a) {
     const int c1 = imin(N, c0 + a.chunk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
-    const int x = wave % 3;                           // softmax kind of this wave
+    const int x = __builtin_amdgcn_readfirstlane(wave % 3);   // softmax kind of this wave (wave-uniform)
     const size_t head_off = (size_t)bh * N * D;
     const uint16_t* kh = a.k + head_off;
     const uint16_t* vh = a.v + head_off;
@@ -97,72 +103,97 @@ __global__ __launch_bounds__(QBLK * 3 * 64) void route_partial_kernel(RArgs a) {
     }
     __syncthreads();
 
-    for (int s = 0; s < steps; ++s) {
-        const char* stg = smem + (s & 1) * St::STAGE;
-        const int kb0 = c0 + s * KSUB;
-        f32x16 sacc[KBLK];
+    // 64-bit keep mask over keys kb0 .. kb0+63 for this lane's sample under softmax kind X
+    // (frame-major coordinates), keys at or past the chunk end excluded
+    auto keep_bits = [&](auto X, int kb0) __attribute__((always_inline)) {
+        uint64_t m = window_bits(kb0, c1, kb0);
+        if constexpr (decltype(X)::value == 1) {
+            m &= window_bits(rks.a0, rks.b0, kb0) | window_bits(rks.a1, rks.b1, kb0);
+        } else if constexpr (decltype(X)::value == 2) {
+            // sink frames whole; in every other frame the positions within bt of the sample's
+            uint64_t t = 0;
+            const int f0 = kb0 / g.S, f1 = imin((kb0 + KSUB - 1) / g.S, g.F - 1);
+            for (int f = f0; f <= f1; ++f) {
+                const int fs = f * g.S;
+                t |= f < g.k ? window_bits(fs, fs + g.S, kb0)
+                             : window_bits(fs + imax((int)sq - g.bt, 0), fs + imin((int)sq + g.bt + 1, g.S), kb0);
+            }
+            m &= t;
+        }
+        return m;
+    };
+    auto run = [&](auto X) __attribute__((always_inline)) {
+        for (int s = 0; s < steps; ++s) {
+            const char* stg = smem + (s & 1) * St::STAGE;
+            const int kb0 = c0 + s * KSUB;
+            f32x16 sacc[KBLK];
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b) sacc[b] = f32x16{};
+            for (int b = 0; b < KBLK; ++b) sacc[b] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
+            for (int c = 0; c < DC; ++c)
 #pragma unroll
-            for (int b = 0; b < KBLK; ++b)
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(St::a_k(stg, b, c, l32, h), qreg[c], sacc[b], 0, 0, 0);
+                for (int b = 0; b < KBLK; ++b)
+                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(St::a_k(stg, b, c, l32, h), qreg[c], sacc[b], 0, 0, 0);
 
-        // this wave's mask, in frame-major coordinates; keys past the chunk are excluded
-        float mx = -INFINITY;
+            // mask by a bit test per score: bit acc_key(b, i, 0) - 32 b of word b, after a shift
+            // that puts this half-wave's keys at acc_key(b, i, 0)
+            const uint64_t m = keep_bits(X, kb0) >> acc_key(0, 0, h);
+            const uint32_t mw[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
+            float mx = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < KBLK; ++b) {
+            for (int b = 0; b < KBLK; ++b) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = kb0 + acc_key(b, i, h);
-                bool keep = j < c1;
-                if (x == 1) {
-                    keep = keep && row_keeps(g, rks, j);
-                } else if (x == 2) {
-                    uint32_t fk, sk;
-                    g.divS.divmod((uint32_t)(j < N ? j : 0), fk, sk);
-                    const int ds = (int)sk - (int)sq;
-                    keep = keep && ((int)fk < g.k || (ds <= g.bt && -ds <= g.bt));
+                for (int i = 0; i < 16; ++i) {
+                    const int pos = acc_key(b, i, 0) - 32 * b;
+                    if (!((mw[b] >> pos) & 1u)) sacc[b][i] = -INFINITY;
+                    mx = fmaxf(mx, sacc[b][i]);
                 }
-                if (!keep) sacc[b][i] = -INFINITY;
-                mx = fmaxf(mx, sacc[b][i]);
             }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow, mx);
-        const float base = mnew == -INFINITY ? 0.f : mnew * a.c2;
-        const float alpha = __builtin_amdgcn_exp2f(mrow * a.c2 - base);
-        mrow = mnew;
-        lrow *= alpha;
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mrow, mx);
+            const float base = mnew == -INFINITY ? 0.f : mnew * a.c2;
+            const float alpha = __builtin_amdgcn_exp2f(mrow * a.c2 - base);
+            mrow = mnew;
+            lrow *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            const int vlo = St::v_lane_off(lane);
 #pragma unroll
-        for (int m16 = 0; m16 < KSUB / 16; ++m16) {
-            // registers 8*(m16%2) .. +7 of key block m16/2 hold keys 16*m16 + 8h .. +7
-            bf16x8 hi8, lo8;
+            for (int m16 = 0; m16 < KSUB / 16; ++m16) {
+                // registers 8*(m16%2) .. +7 of key block m16/2 hold keys 16*m16 + 8h .. +7
+                bf16x8 hi8, lo8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[m16 >> 1][8 * (m16 & 1) + e], a.c2, -base));
-                lrow += p;
-                const __bf16 ph = (__bf16)p;
-                hi8[e] = ph;
-                lo8[e] = (__bf16)(p - (float)ph);
+                for (int e = 0; e < 8; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[m16 >> 1][8 * (m16 & 1) + e], a.c2, -base));
+                    lrow += p;
+                    const __bf16 ph = (__bf16)p;
+                    hi8[e] = ph;
+                    lo8[e] = (__bf16)(p - (float)ph);
+                }
+                bf16x8 av[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) av[db] = St::a_v(stg, db, m16, vlo);
+                // the high parts of all dimension blocks, then the low parts: no product
+                // waits on the one just before it
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], hi8, oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], lo8, oacc[db], 0, 0, 0);
             }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 av = St::a_v(stg, db, m16, St::v_lane_off(lane));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, hi8, oacc[db], 0, 0, 0);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, lo8, oacc[db], 0, 0, 0);
-            }
-        }
 
-        if (s + 1 < steps) {
-            st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
-            if (s + 2 < steps) st.load(kh, vh, kb0 + 2 * KSUB, N, ident, tid);
+            if (s + 1 < steps) {
+                st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
+                if (s + 2 < steps) st.load(kh, vh, kb0 + 2 * KSUB, N, ident, tid);
+            }
+            __syncthreads();
         }
-        __syncthreads();
-    }
+    };
+    // the kind is uniform per wave, so each wave runs one specialised loop (all pass the same barriers)
+    if (x == 0) run(std::integral_constant<int, 0>{});
+    else if (x == 1) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 2>{});
 
     // ---- partial of this (sample, kind): max in the log2 domain, sum, unnormalised output
     const float lt = lrow + __shfl_xor(lrow, 32);

@@ -33,6 +33,14 @@ __device__ __forceinline__ int pi32(int r) { return (r & ~12) | ((r & 4) << 1) |
 // Key index held by accumulator register i of a lane in half h of 32-key block b.
 __device__ __forceinline__ int acc_key(int b, int i, int h) { return b * 32 + pi32(8 * (i >> 2) + 4 * h + (i & 3)); }
 
+// Bits [a - kb0, b - kb0) of a 64-bit mask over keys kb0 .. kb0+63 (clamped).
+__device__ __forceinline__ uint64_t window_bits(int a, int b, int kb0) {
+    const int lo = imin(imax(a - kb0, 0), 64), hi = imin(imax(b - kb0, 0), 64);
+    const uint64_t below_hi = hi >= 64 ? ~0ull : (1ull << hi) - 1;
+    const uint64_t below_lo = lo >= 64 ? ~0ull : (1ull << lo) - 1;
+    return below_hi & ~below_lo;
+}
+
 // Raw buffer resource over bytes bytes from p (no stride, gfx9 data format):
 // buffer loads at offsets at or past bytes return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, int bytes) {
