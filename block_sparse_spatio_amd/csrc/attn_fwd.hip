@@ -473,8 +473,11 @@ void attn_fwd_kernel(KArgs a) {
                 Sp::template softmax<false>(sacc, preg, ws, rk, a, 0, lane, hook);
             Sp::fence(preg, ws);
         };
-        // products of step s: PV of step s-1 (if any) and QK^T of step s (if any)
+        // products of step s: PV of step s-1 (if any) and QK^T of step s (if any),
+        // issued at raised wave priority so that the SIMD's arbiter prefers the
+        // matrix wave over its partner's vector work
         auto prod = [&](auto both, int s) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_setprio(1);
             if constexpr (decltype(both)::value)
                 Sp::template products<true, true>(stage(s - 1), stage(s), preg, qreg, sacc, ws, lane);
             else if (s == 0)
@@ -482,6 +485,7 @@ void attn_fwd_kernel(KArgs a) {
             else
                 Sp::template products<true, false>(stage(s - 1), nullptr, preg, qreg, sacc, ws, lane);
             Sp::fence(sacc);
+            __builtin_amdgcn_s_setprio(0);
         };
         using Both = std::true_type;
         using One = std::false_type;
