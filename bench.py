@@ -54,7 +54,7 @@ def main():
     import torch
 
     import block_sparse_spatio_amd as B
-    from synth import HEADLINE, planted_qkv, sample_indices
+    from synth import HEADLINE, P1440, planted_qkv, sample_indices
 
     w = HEADLINE
     dev = torch.device("cuda:0")
@@ -171,6 +171,7 @@ def main():
         extras["permute_path_ms (3 permutes + attention + unpermute)"] = round(3 * t_perm + t_attn + t_unperm, 4)
         for bq_x in (128, 256, 512):
             extras[f"exact_bq{bq_x}_ms"] = round(attn_with(B.MAP_EXACT, bq_x), 4)
+        extras["layer_1440p"] = layer_1440p(B, torch, dev, P1440)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -239,6 +240,56 @@ def main():
         "context_tpu_v6e_ms (pages, isolated kernel, other hardware)": PAGES_TPU_V6E_MS,
     }
     print(json.dumps(out), flush=True)
+
+
+def layer_1440p(B, torch, dev, w):
+    """The 302,400-token layer end to end: routing on 64 samples, tile map, permutation of Q, K, V,
+    exact sparse attention, unpermutation (HIP events; a few calls, inputs resident)."""
+    from synth import planted_qkv, sample_indices
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    q, k, v = planted_qkv(1, w.F, w.H, w.W, w.d, w.kinds, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    idx = sample_indices(w.N, w.n_samples, seed=0).to(dev)
+    ws = torch.empty(B.svga_route_workspace_bytes(1, w.heads, geom, w.d, w.n_samples), dtype=torch.uint8, device=dev)
+    flags = torch.empty(1, w.heads, dtype=torch.uint8, device=dev)
+    err = torch.empty(1, w.heads, 2, dtype=torch.float32, device=dev)
+    off = B.svga_tilemap_layout(geom, w.bq, w.bkv)
+    tmap = torch.empty(off.total, dtype=torch.uint8, device=dev)
+    qp, kp, vp, op, o = (torch.empty_like(qd) for _ in range(5))
+    mode = B.MAP_EXACT
+
+    def parts():
+        return [lambda: B.svga_route_heads(qd, kd, vd, geom, mask, idx, workspace=ws, flags_out=flags, err_out=err),
+                lambda: B.svga_build_tilemap(geom, mask, w.bq, w.bkv, mode, out=tmap),
+                lambda: (B.svga_permute(qd, flags, geom, mask, out=qp), B.svga_permute(kd, flags, geom, mask, out=kp),
+                         B.svga_permute(vd, flags, geom, mask, out=vp)),
+                lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, w.bq, w.bkv, mode, out=op),
+                lambda: B.svga_unpermute(op, flags, geom, mask, out=o)]
+
+    for f in parts():
+        f()
+    torch.cuda.synchronize()
+    reps = 3
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+          for _ in range(reps)]
+    for r in range(reps):
+        for (a, b), f in zip(ev[r], parts()):
+            a.record()
+            f()
+            b.record()
+    torch.cuda.synchronize()
+    ms = [sum(a.elapsed_time(b) for a, b in ev[r]) for r in range(reps)]
+    each = [sum(ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(reps)) / reps for i in range(5)]
+    host_map = B.tilemap_views(tmap.cpu().numpy(), geom, w.bq, w.bkv)
+    fl = flags.cpu().numpy()[0]
+    n_exec = int(sum(host_map["n_full"][kk].sum() + host_map["n_bnd"][kk].sum() for kk in fl))
+    return {"workload": "302,400 tokens (21x90x160), 10 heads, d=128, routed on 64 samples, EXACT 256x128",
+            "step_ms": round(sorted(ms)[reps // 2], 3), "route_ms": round(each[0], 4), "tilemap_ms": round(each[1], 4),
+            "permute_qkv_ms": round(each[2], 4), "attn_ms": round(each[3], 3), "unpermute_ms": round(each[4], 4),
+            "routed_flags": fl.tolist(),
+            "attn_executed_tile_tflops": round(4.0 * w.d * w.bq * w.bkv * n_exec / (each[3] * 1e-3) / 1e12, 1)}
 
 
 def counter_record(name, key, mode, bq, bkv):
