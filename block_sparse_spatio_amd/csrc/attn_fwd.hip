@@ -35,8 +35,8 @@
 //   registers and load the step after, one chunk between blocks of
 //   exponentials, so the step top is a bare barrier and the products of
 //   waves 0-3 never wait behind load issue. Smaller workgroups
-//   have no partner wave, and 64-row waves no registers to spare for the
-//   second phase's state: they run QK^T, softmax and PV in turn.
+//   have no partner wave: they run QK^T, softmax and PV in turn. 512-row
+//   query tiles run as two 256-row workgroups.
 // * Lazy rescaling: a row keeps its exponent base until its running max
 //   exceeds the base by more than 2^8 in probability scale; only then are the
 //   output accumulator and the row sum rescaled. The final normalisation uses
@@ -71,6 +71,7 @@ struct KArgs {
     Geo g;
     int32_t tq, tk, bkv;
     int32_t exact;          // 1: exact mask on boundary tiles, 0: padding only
+    int32_t qparts;         // workgroups per map query tile (its rows split in parts of this kernel's BQ)
     int32_t total;
     float c2;               // softmax_scale * log2(e)
     float scale;
@@ -324,8 +325,11 @@ void attn_fwd_kernel(KArgs a) {
     const int id = blockIdx.x;
     const int logical = id;
     if (logical >= a.total) return;
-    const int bh = logical / a.tq;
-    const int qt = logical - bh * a.tq;
+    const int per_bh = a.tq * a.qparts;
+    const int bh = logical / per_bh;
+    const int qrem = logical - bh * per_bh;
+    const int qt = qrem / a.qparts;                                   // query tile of the map
+    const int row0 = qt * BQ * a.qparts + (qrem - qt * a.qparts) * BQ;   // first row of this part
     const int N = a.g.N;
     const int kind = a.flags[bh] ? SVGA_KIND_TEMPORAL : SVGA_KIND_SPATIAL;
     const bool gat = GATHER && kind == SVGA_KIND_TEMPORAL;
@@ -354,7 +358,7 @@ void attn_fwd_kernel(KArgs a) {
     RowKeys rk[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int row = qt * BQ + (wave * QB + qb) * 32 + l32;
+        const int row = row0 + (wave * QB + qb) * 32 + l32;
         if (row < N) {
             const int qsrc = gat ? temporal_src(g, row) : row;
             const bf16x8* p = reinterpret_cast<const bf16x8*>(qh + (size_t)qsrc * D + 8 * h);
@@ -552,7 +556,7 @@ void attn_fwd_kernel(KArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const float lt = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int row = qt * BQ + (wave * QB + qb) * 32 + l32;
+        const int row = row0 + (wave * QB + qb) * 32 + l32;
         if (row < N) {
             const int orow = gat ? temporal_src(g, row) : row;
             uint16_t* op = oh + (size_t)orow * D;
@@ -587,7 +591,9 @@ hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// bq -> (QB, WAVES): 32 -> (1,1), 64 -> (1,2), 128 -> (1,4), 256 -> (1,8), 512 -> (2,8).
+// bq -> (QB, WAVES): 32 -> (1,1), 64 -> (1,2), 128 -> (1,4), 256 -> (1,8); a 512-row
+// query tile runs as two 256-row workgroups that walk the same tile lists (64-row
+// waves do not fit two per SIMD without spilling).
 // KSUB = 64 when bkv is a multiple of 64, else 32.
 template <int D>
 hipError_t dispatch(const KArgs& k, int bq, int ksub, bool gather, hipStream_t stream, bool* sup) {
@@ -597,13 +603,24 @@ hipError_t dispatch(const KArgs& k, int bq, int ksub, bool gather, hipStream_t s
         if (bq == 64) return launch_one<D, 1, 2, 64>(k, gather, stream);
         if (bq == 128) return launch_one<D, 1, 4, 64>(k, gather, stream);
         if (bq == 256) return launch_one<D, 1, 8, 64>(k, gather, stream);
-        if (bq == 512) return launch_one<D, 2, 8, 64>(k, gather, stream);
+        if (bq == 512) {
+            // two 256-row parts per 512-row query tile, each walking that tile's lists
+            KArgs k2 = k;
+            k2.qparts = 2;
+            k2.total = k.total * 2;
+            return launch_one<D, 1, 8, 64>(k2, gather, stream);
+        }
     } else {
         if (bq == 32) return launch_one<D, 1, 1, 32>(k, gather, stream);
         if (bq == 64) return launch_one<D, 1, 2, 32>(k, gather, stream);
         if (bq == 128) return launch_one<D, 1, 4, 32>(k, gather, stream);
         if (bq == 256) return launch_one<D, 1, 8, 32>(k, gather, stream);
-        if (bq == 512) return launch_one<D, 2, 8, 32>(k, gather, stream);
+        if (bq == 512) {
+            KArgs k2 = k;
+            k2.qparts = 2;
+            k2.total = k.total * 2;
+            return launch_one<D, 1, 8, 32>(k2, gather, stream);
+        }
     }
     *sup = false;
     return hipSuccess;
@@ -635,6 +652,7 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* suppor
     k.tk = a.L.tk;
     k.bkv = a.bkv;
     k.exact = (a.mode == SVGA_MAP_NAIVE || a.mode == SVGA_MAP_EXACT) ? 1 : 0;
+    k.qparts = 1;
     k.total = a.BH * a.L.tq;
     k.c2 = a.scale * 1.4426950408889634f;
     k.scale = a.scale;

@@ -211,8 +211,8 @@ svga_status svga_route_heads(const void* d_q, const void* d_k, const void* d_v,
  *   scores (natural log; -inf for a row with no kept key), rows in O's
  *   order; or NULL.
  * Rows with no kept key get O = 0.
- * Supported: head_dim 64 or 128; bq in {32, 64, 128, 256, 512} (head_dim 64:
- * up to 256); bkv a multiple of 64 up to 512, or 32 with bq 32. One head of
+ * Supported: head_dim 64 or 128; bq in {32, 64, 128, 256, 512}; bkv a
+ * multiple of 32 from 32 to 512. One head of
  * K or V (N * head_dim * 2 bytes) must stay below 2^31 bytes, which the
  * tile-count limit (tq * tk below 2^28) already implies for these tiles.
  * d_o must not alias d_q, d_k or d_v. */

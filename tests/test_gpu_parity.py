@@ -158,7 +158,8 @@ def test_attention_tiny(dev, mode, src_dtype):
             assert np.abs(lse[0, h].numpy() - ref_lse).max() < 1e-3
 
 
-@pytest.mark.parametrize("tiles", [(128, 128), (256, 128), (64, 64), (128, 64), (32, 32), (512, 128), (256, 256)])
+@pytest.mark.parametrize("tiles", [(128, 128), (256, 128), (64, 64), (128, 64), (32, 32), (512, 128), (256, 256),
+                                   (256, 96), (512, 32)])
 @pytest.mark.parametrize("mode", [0, 2, 3])
 def test_attention_small(dev, tiles, mode):
     w = SMALL
