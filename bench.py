@@ -76,6 +76,7 @@ def main():
     off = B.svga_tilemap_layout(geom, bq, bkv)
     tmap = torch.empty(off.total, dtype=torch.uint8, device=dev)
     qp, kp, vp, op, o = (torch.empty_like(qd) for _ in range(5))
+    aws = torch.empty(B.svga_attn_workspace_bytes(), dtype=torch.uint8, device=dev)   # persistent workgroups
 
     def step():
         B.svga_route_heads(qd, kd, vd, geom, mask, idx, workspace=ws, flags_out=flags, err_out=err)
@@ -83,7 +84,7 @@ def main():
         B.svga_permute(qd, flags, geom, mask, out=qp)
         B.svga_permute(kd, flags, geom, mask, out=kp)
         B.svga_permute(vd, flags, geom, mask, out=vp)
-        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op)
+        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op, workspace=aws)
         B.svga_unpermute(op, flags, geom, mask, out=o)
 
     log("bench: warmup")
@@ -120,14 +121,14 @@ def main():
     t_map = timed(lambda: B.svga_build_tilemap(geom, mask, bq, bkv, mode, out=tmap), reps)
     t_perm = timed(lambda: B.svga_permute(kd, flags, geom, mask, out=kp), reps)
     t_unperm = timed(lambda: B.svga_unpermute(op, flags, geom, mask, out=o), reps)
-    t_attn = timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op), reps)
+    t_attn = timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op, workspace=aws), reps)
     # latency: median of 20 individually event-timed calls after 5 warm-ups
     for _ in range(5):
-        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op)
+        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op, workspace=aws)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
     for a_, b_ in ev:
         a_.record()
-        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op)
+        B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, bq, bkv, mode, out=op, workspace=aws)
         b_.record()
     torch.cuda.synchronize()
     t_attn_median = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
@@ -157,9 +158,9 @@ def main():
             m = B.svga_build_tilemap(geom, mask, bq_x, bkv, mode_x)
             if gather:
                 return timed(lambda: B.svga_sparse_attn_fwd(qd, kd, vd, flags, m, geom, mask, bq_x, bkv, mode_x,
-                                                            gather_temporal=True, out=op), reps)
-            return timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, m, geom, mask, bq_x, bkv, mode_x, out=op),
-                         reps)
+                                                            gather_temporal=True, out=op, workspace=aws), reps)
+            return timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, m, geom, mask, bq_x, bkv, mode_x, out=op,
+                                                        workspace=aws), reps)
         t_dense = attn_with(B.MAP_DENSE, bq)
         extras["dense_map_ms (B0)"] = round(t_dense, 4)
         extras["dense_map_tflops"] = round(4.0 * d * N * N * w.heads / (t_dense * 1e-3) / 1e12, 1)
@@ -171,7 +172,7 @@ def main():
         extras["permute_path_ms (3 permutes + attention + unpermute)"] = round(3 * t_perm + t_attn + t_unperm, 4)
         for bq_x in (128, 256, 512):
             extras[f"exact_bq{bq_x}_ms"] = round(attn_with(B.MAP_EXACT, bq_x), 4)
-        extras["layer_1440p"] = layer_1440p(B, torch, dev, P1440)
+        extras["layer_1440p"] = layer_1440p(B, torch, dev, P1440, aws)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -197,6 +198,7 @@ def main():
                         "frames) + 5 temporal heads (window 644), first-frame sink; step = route(64 samples) + "
                         f"tile map + permute QKV + {args.mode} attention + unpermute",
             "tiles": f"{bq}x{bkv}",
+            "launch": "persistent workgroups taking query tiles from a counter (svga_sparse_attn_fwd_ws)",
             "mode": args.mode,
         },
         "roofline": {
@@ -242,7 +244,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def layer_1440p(B, torch, dev, w):
+def layer_1440p(B, torch, dev, w, aws):
     """The 302,400-token layer end to end: routing on 64 samples, tile map, permutation of Q, K, V,
     exact sparse attention, unpermutation (HIP events; a few calls, inputs resident)."""
     from synth import planted_qkv, sample_indices
@@ -265,7 +267,8 @@ def layer_1440p(B, torch, dev, w):
                 lambda: B.svga_build_tilemap(geom, mask, w.bq, w.bkv, mode, out=tmap),
                 lambda: (B.svga_permute(qd, flags, geom, mask, out=qp), B.svga_permute(kd, flags, geom, mask, out=kp),
                          B.svga_permute(vd, flags, geom, mask, out=vp)),
-                lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, w.bq, w.bkv, mode, out=op),
+                lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, tmap, geom, mask, w.bq, w.bkv, mode, out=op,
+                                               workspace=aws),
                 lambda: B.svga_unpermute(op, flags, geom, mask, out=o)]
 
     for f in parts():

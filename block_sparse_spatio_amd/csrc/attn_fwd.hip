@@ -72,7 +72,8 @@ struct KArgs {
     int32_t tq, tk, bkv;
     int32_t exact;          // 1: exact mask on boundary tiles, 0: padding only
     int32_t qparts;         // workgroups per map query tile (its rows split in parts of this kernel's BQ)
-    int32_t total;
+    int32_t total;          // work items: BH * tq * qparts
+    int32_t* counter;       // persistent mode: next work item (zeroed before the launch); else null
     float c2;               // softmax_scale * log2(e)
     float scale;
 };
@@ -310,9 +311,9 @@ __device__ __forceinline__ void phase_barrier() {
 
 // QB = 1: at most 256 registers per wave, so two waves share each SIMD (two
 // 4-wave workgroups, or one 8-wave workgroup, per CU).
+// One work item: the rows of (batch*head, query tile, part) `logical`.
 template <int D, int QB, int WAVES, int KSUB, bool GATHER>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
-void attn_fwd_kernel(KArgs a) {
+__device__ __forceinline__ void attn_item(const KArgs& a, const int logical, char* smem) {
     constexpr bool PINGPONG = WAVES == 8 && QB == 1;
     constexpr int NT = WAVES * 64;
     constexpr int BQ = WAVES * QB * 32;
@@ -320,10 +321,6 @@ void attn_fwd_kernel(KArgs a) {
     constexpr int DB = D / 32;
     using St = Stager<D, KSUB, NT>;
     using Sp = Step<D, QB, KSUB, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[(PINGPONG ? 4 : 2) * St::STAGE];
-
-    const int id = blockIdx.x;
-    const int logical = id;
     if (logical >= a.total) return;
     const int per_bh = a.tq * a.qparts;
     const int bh = logical / per_bh;
@@ -581,9 +578,54 @@ void attn_fwd_kernel(KArgs a) {
     }
 }
 
+// Without a counter, one workgroup per work item in index order. With one,
+// persistent workgroups (one per CU) take the next item from the counter until
+// none is left: no workgroup launch between items, and a free CU takes work at
+// once instead of waiting while the in-order dispatcher blocks on a full XCD.
+template <int D, int QB, int WAVES, int KSUB, bool GATHER>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
+void attn_fwd_kernel(KArgs a) {
+    constexpr bool PINGPONG = WAVES == 8 && QB == 1;
+    using St = Stager<D, KSUB, WAVES * 64>;
+    __shared__ __attribute__((aligned(16))) char smem[(PINGPONG ? 4 : 2) * St::STAGE];
+    __shared__ int next;
+    if (!a.counter) {
+        attn_item<D, QB, WAVES, KSUB, GATHER>(a, blockIdx.x, smem);
+        return;
+    }
+    for (;;) {
+        if (threadIdx.x == 0) next = atomicAdd(a.counter, 1);
+        __syncthreads();
+        const int t = next;
+        __syncthreads();   // every wave has read `next` before it changes; the last item's LDS reads are done
+        if (t >= a.total) break;
+        attn_item<D, QB, WAVES, KSUB, GATHER>(a, t, smem);
+    }
+}
+
+__global__ void zero_counter_kernel(int32_t* c) {
+    if (threadIdx.x == 0) *c = 0;
+}
+
 template <int D, int QB, int WAVES, int KSUB>
 hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
-    dim3 grid((unsigned)k.total);
+    unsigned nwg = (unsigned)k.total;
+    if (k.counter) {
+        // as many workgroups as can be resident at once
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                             &per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, true>, WAVES * 64, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                             &per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, false>, WAVES * 64, 0);
+        if (e != hipSuccess) return e;
+        nwg = (unsigned)imin(k.total, cus * imax(per_cu, 1));
+        hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, stream, k.counter);
+    }
+    if (nwg == 0) return hipGetLastError();
+    dim3 grid(nwg);
     if (gather)
         hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, true>), grid, dim3(WAVES * 64), 0, stream, k);
     else
@@ -654,6 +696,7 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* suppor
     k.exact = (a.mode == SVGA_MAP_NAIVE || a.mode == SVGA_MAP_EXACT) ? 1 : 0;
     k.qparts = 1;
     k.total = a.BH * a.L.tq;
+    k.counter = a.counter;
     k.c2 = a.scale * 1.4426950408889634f;
     k.scale = a.scale;
     const int ksub = a.bkv % 64 == 0 ? 64 : 32;

@@ -238,8 +238,10 @@ struct AttnLaunch {
     int32_t BH;            // B * n_heads
     int32_t head_dim, bq, bkv, mode, gather;
     float scale;
+    int32_t* counter;      // persistent workgroups: work counter in the caller's workspace, or null
 };
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* supported);
+constexpr size_t kAttnWorkspaceBytes = 256;   // the work counter, padded
 bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv);
 
 hipError_t launch_permute(const void* in, void* out, const uint8_t* flags, int32_t BH, const Geo& g,

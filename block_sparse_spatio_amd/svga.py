@@ -174,9 +174,18 @@ def svga_route_heads(q, k, v, geom, mask, sample_idx, softmax_scale=None, worksp
     return flags_out, err_out
 
 
+def svga_attn_workspace_bytes():
+    """Device workspace bytes of svga_sparse_attn_fwd with a workspace (persistent workgroups)."""
+    n = ctypes.c_size_t()
+    _check(lib().svga_attn_workspace_bytes(ctypes.byref(n)))
+    return n.value
+
+
 def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, softmax_scale=None,
-                         gather_temporal=False, out=None, lse=None, want_lse=False, stream=None):
-    """Block-sparse attention forward. Returns (out, lse); lse is None unless requested."""
+                         gather_temporal=False, out=None, lse=None, want_lse=False, workspace=None, stream=None):
+    """Block-sparse attention forward. Returns (out, lse); lse is None unless requested.
+    With `workspace` (a device tensor of at least svga_attn_workspace_bytes() bytes) the call runs
+    persistent workgroups (svga_sparse_attn_fwd_ws); the results are the same bits."""
     _qkv_check(q, k, v)
     B, H, N, d = q.shape
     out = torch.empty_like(q) if out is None else out
@@ -184,8 +193,12 @@ def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, sof
     if lse is None and want_lse:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    _check(lib().svga_sparse_attn_fwd(_vp(q), _vp(k), _vp(v), _vp(out), _vp(lse), B, H, ctypes.byref(_geom(geom)),
-                                      ctypes.byref(_mask(mask)), d, float(scale), _vp(flags), _vp(tilemap),
-                                      tilemap.numel() * tilemap.element_size(), int(bq), int(bkv), _mode(mode),
-                                      1 if gather_temporal else 0, _stream(stream)))
+    args = (_vp(q), _vp(k), _vp(v), _vp(out), _vp(lse), B, H, ctypes.byref(_geom(geom)), ctypes.byref(_mask(mask)), d,
+            float(scale), _vp(flags), _vp(tilemap), tilemap.numel() * tilemap.element_size(), int(bq), int(bkv),
+            _mode(mode), 1 if gather_temporal else 0)
+    if workspace is None:
+        _check(lib().svga_sparse_attn_fwd(*args, _stream(stream)))
+    else:
+        _check(lib().svga_sparse_attn_fwd_ws(*args, _vp(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))
     return out, lse

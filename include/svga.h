@@ -224,6 +224,28 @@ svga_status svga_sparse_attn_fwd(const void* d_q, const void* d_k, const void* d
                                  int32_t bq, int32_t bkv, int32_t mode,
                                  int32_t gather_temporal, void* stream);
 
+/* Device workspace bytes that svga_sparse_attn_fwd_ws needs (a work counter). */
+svga_status svga_attn_workspace_bytes(size_t* bytes);
+
+/* svga_sparse_attn_fwd with persistent workgroups: as many workgroups as the
+ * device holds at once, each taking the next (batch, head, query tile) from a
+ * counter in d_workspace until none is left (no workgroup launch between
+ * query tiles, and no CU idles while the in-order dispatcher waits on a busy
+ * one). Same arguments, same results bit for bit, plus:
+ * d_workspace: caller-owned device memory, at least svga_attn_workspace_bytes
+ *   bytes, 4-byte aligned; its content on entry does not matter (the call
+ *   clears it on the stream first) and is undefined afterwards.
+ *   SVGA_EINVAL if NULL or misaligned, SVGA_ECAPACITY if too small.
+ * Calls that share one workspace must not overlap (one stream, or ordered). */
+svga_status svga_sparse_attn_fwd_ws(const void* d_q, const void* d_k, const void* d_v,
+                                    void* d_o, float* d_lse,
+                                    int32_t B, int32_t n_heads, const svga_geom* geom,
+                                    const svga_mask* mask, int32_t head_dim, float softmax_scale,
+                                    const uint8_t* d_flags, const void* d_map, size_t map_bytes,
+                                    int32_t bq, int32_t bkv, int32_t mode,
+                                    int32_t gather_temporal, void* d_workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

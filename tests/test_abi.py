@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == len(_lib.SIGNATURES) == 11
+    assert len(names) == len(_lib.SIGNATURES) == 13
     assert set(names) == set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(L, n), n
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.svga_version() == 100
+    assert L.svga_version() == 101
     assert L.svga_status_string(0) == b"ok"
     assert L.svga_status_string(-3) == b"buffer too small"
 
@@ -100,6 +100,16 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.svga_sparse_attn_fwd(*a, o, None, 1, 2, g, m, 64, ctypes.c_float(-1.0), FAKE, FAKE, 1 << 20, 32, 32, 2, 0, None) == -1
     assert L.svga_sparse_attn_fwd(*a, o, None, 1, 2, g, m, 64, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, 32, 32, 2, 2, None) == -1
     assert L.svga_sparse_attn_fwd(*a, o, None, 1, 2, g, m, 64, ctypes.c_float(0.1), None, FAKE, 1 << 20, 32, 32, 2, 0, None) == -1
+    # persistent variant: workspace size query, NULL / small / misaligned workspace, then the common checks
+    n = ctypes.c_size_t()
+    assert L.svga_attn_workspace_bytes(ctypes.byref(n)) == 0 and n.value >= 4
+    assert L.svga_attn_workspace_bytes(None) == -1
+    common = (*a, o, None, 1, 2, g, m, 64, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, 32, 32, 2, 0)
+    assert L.svga_sparse_attn_fwd_ws(*common, None, n.value, None) == -1
+    assert L.svga_sparse_attn_fwd_ws(*common, FAKE, n.value - 1, None) == -3
+    assert L.svga_sparse_attn_fwd_ws(*common, ctypes.c_void_p(0x1002), n.value, None) == -1
+    bad = (*a, o, None, 1, 2, g, m, 96, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, 32, 32, 2, 0)
+    assert L.svga_sparse_attn_fwd_ws(*bad, FAKE, n.value, None) == -2
 
 
 def test_python_binding_raises_with_message():

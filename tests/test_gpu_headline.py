@@ -171,6 +171,22 @@ def test_headline_gather_equals_permute_bitwise(dev, headline):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_headline_persistent_equals_plain_bitwise(dev, headline):
+    """The benchmark's persistent launch gives the same bits as one workgroup per query tile."""
+    w, q, k, v, qd, kd, vd = headline
+    geom, mask = geom_mask(w)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say("headline persistent vs plain")
+    tm = B.svga_build_tilemap(geom, mask, 256, 128, B.MAP_EXACT, device=dev)
+    ws = torch.zeros(B.svga_attn_workspace_bytes(), dtype=torch.uint8, device=dev)
+    a, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, 256, 128, B.MAP_EXACT)
+    b, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, 256, 128, B.MAP_EXACT, workspace=ws)
+    c, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, 256, 128, B.MAP_EXACT, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
 def test_1440p_routing_and_attention(dev):
     """Routing on 64 sampled queries at 302,400 tokens finds the planted head kinds; the routed
     pipeline matches the oracle on sampled rows."""

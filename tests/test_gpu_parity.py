@@ -177,6 +177,31 @@ def test_attention_small(dev, tiles, mode):
         assert_close(o[0, h, rows].float().numpy(), ref, f"head {h}")
 
 
+@pytest.mark.parametrize("tiles,mode,gather", [((256, 128), 2, False), ((256, 128), 3, True), ((512, 128), 2, False),
+                                               ((128, 64), 0, False), ((32, 32), 1, False), ((256, 96), 2, True)])
+def test_persistent_equals_plain_bitwise(dev, tiles, mode, gather):
+    """Persistent workgroups (the workspace entry point) give the same output and LSE bits as one workgroup
+    per query tile; the workspace is reused (with garbage in it) by a second, smaller call."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    bq, bkv = tiles
+    say(f"persistent tiles={tiles} mode={mode} gather={gather}")
+    q, k, v = (x.to(dev) for x in normal_qkv(2, w.heads, w.N, w.d, seed=4))
+    flags = torch.tensor([list(w.kinds)] * 2, dtype=torch.uint8, device=dev)
+    tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
+    ws = torch.full((B.svga_attn_workspace_bytes(),), 0x5A, dtype=torch.uint8, device=dev)
+    for batch in (2, 1):
+        qb, kb, vb, fb = q[:batch], k[:batch], v[:batch], flags[:batch]
+        a, la = B.svga_sparse_attn_fwd(qb, kb, vb, fb, tm, geom, mask, bq, bkv, mode, gather_temporal=gather,
+                                       want_lse=True)
+        b, lb = B.svga_sparse_attn_fwd(qb, kb, vb, fb, tm, geom, mask, bq, bkv, mode, gather_temporal=gather,
+                                       want_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(la.view(torch.int32), lb.view(torch.int32))
+
+
 def test_gather_equals_permute_path_bitwise(dev):
     """In-kernel gather of temporal rows gives the same bits as permute -> attention -> unpermute."""
     w = SMALL
