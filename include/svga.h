@@ -227,8 +227,10 @@ svga_status svga_sparse_attn_fwd(const void* d_q, const void* d_k, const void* d
 /* Device workspace bytes that svga_sparse_attn_fwd_ws needs (a work counter). */
 svga_status svga_attn_workspace_bytes(size_t* bytes);
 
-/* svga_sparse_attn_fwd with persistent workgroups: as many workgroups as the
- * device holds at once, each taking the next (batch, head, query tile) from a
+/* The operation of svga_sparse_attn_fwd (ASTA section "Logical sparsity is
+ * not physical sparsity": the tile walk over each query tile's FULL, then
+ * BOUNDARY key tiles), launched as persistent workgroups: as many workgroups
+ * as the device holds at once, each taking the next (batch, head, query tile) from a
  * counter in d_workspace until none is left (no workgroup launch between
  * query tiles, and no CU idles while the in-order dispatcher waits on a busy
  * one). Same arguments, same results bit for bit, plus:
