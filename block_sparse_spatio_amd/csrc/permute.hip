@@ -4,15 +4,17 @@
 // "Support dynamic routing with fixed tensor shapes").
 //
 // Both directions are written as gathers: every output row is written once,
-// in order, with 16-byte stores; each input row (head_dim * 2 bytes, 256 B at
-// head_dim 128) is read whole by consecutive lanes. HBM-bound: one read and
-// one write of the tensor.
+// in order, with 16-byte non-temporal stores (streamed past the caches: 6.9
+// against 5.4 TB/s with ordinary stores); each input row (head_dim * 2 bytes,
+// 256 B at head_dim 128) is read whole by consecutive lanes. HBM-bound: one
+// read and one write of the tensor.
 #include "svga_internal.h"
 
 namespace svga {
 
 namespace {
 
+typedef unsigned u32x4nt __attribute__((ext_vector_type(4)));   // for the non-temporal store builtin
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;   // 16-byte vectors per thread, loaded before any store
 
@@ -33,17 +35,17 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const uint4* __restri
         if (temporal) sr = inverse ? temporal_dst(g, sr) : temporal_src(g, sr);
         return src[(int64_t)sr * row_vecs + c];
     };
-    // four independent 16-byte loads in flight per lane, then the stores
-    const uint32_t e0 = base, e1 = base + kThreads, e2 = base + 2 * kThreads, e3 = base + 3 * kThreads;
-    uint4 v0{}, v1{}, v2{}, v3{};
-    if (e0 < hv) v0 = fetch(e0);
-    if (e1 < hv) v1 = fetch(e1);
-    if (e2 < hv) v2 = fetch(e2);
-    if (e3 < hv) v3 = fetch(e3);
-    if (e0 < hv) dst[e0] = v0;
-    if (e1 < hv) dst[e1] = v1;
-    if (e2 < hv) dst[e2] = v2;
-    if (e3 < hv) dst[e3] = v3;
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+        const uint32_t e = base + i * kThreads;
+        v[i] = e < hv ? fetch(e) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+        const uint32_t e = base + i * kThreads;
+        if (e < hv) __builtin_nontemporal_store(__builtin_bit_cast(u32x4nt, v[i]), reinterpret_cast<u32x4nt*>(dst + e));
+    }
 }
 
 }  // namespace
