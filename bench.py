@@ -76,7 +76,8 @@ def main():
     off = B.svga_tilemap_layout(geom, bq, bkv)
     tmap = torch.empty(off.total, dtype=torch.uint8, device=dev)
     qp, kp, vp, op, o = (torch.empty_like(qd) for _ in range(5))
-    aws = torch.empty(B.svga_attn_workspace_bytes(), dtype=torch.uint8, device=dev)   # persistent workgroups
+    # persistent workgroups with the split tail (the size for 256-row workgroups covers every bq)
+    aws = torch.empty(B.svga_attn_split_workspace_bytes(w.d, 512), dtype=torch.uint8, device=dev)
 
     def step():
         B.svga_route_heads(qd, kd, vd, geom, mask, idx, workspace=ws, flags_out=flags, err_out=err)
@@ -198,11 +199,12 @@ def main():
                         "frames) + 5 temporal heads (window 644), first-frame sink; step = route(64 samples) + "
                         f"tile map + permute QKV + {args.mode} attention + unpermute",
             "tiles": f"{bq}x{bkv}",
-            "launch": "persistent workgroups taking query tiles from a counter (svga_sparse_attn_fwd_ws)",
+            "launch": "persistent workgroups taking query tiles from a counter, the last 256 query tiles split "
+                      "in 4 pieces merged by log-sum-exp (svga_sparse_attn_fwd_ws, split-tail workspace)",
             "mode": args.mode,
         },
         "roofline": {
-            "kernel": "attn_fwd_kernel (svga_sparse_attn_fwd)",
+            "kernel": "attn_fwd_kernel + merge_kernel (one svga_sparse_attn_fwd_ws call)",
             "bound": "mfma",
             "achieved": round(tflops_alg, 2),
             "peak": PEAK_BF16_TFLOPS,

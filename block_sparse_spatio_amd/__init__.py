@@ -8,7 +8,7 @@ from .svga import (  # noqa: F401
     SvgaError, make_geom, make_mask, tilemap_views,
     svga_version, svga_tilemap_layout, svga_build_tilemap_host, svga_build_tilemap,
     svga_permute, svga_unpermute, svga_route_workspace_bytes, svga_route_heads, svga_sparse_attn_fwd,
-    svga_attn_workspace_bytes,
+    svga_attn_workspace_bytes, svga_attn_split_workspace_bytes,
     KIND_SPATIAL, KIND_TEMPORAL, TL_SINK_FIRST, TL_LITERAL,
     MAP_DENSE, MAP_NAIVE, MAP_EXACT, MAP_ROUNDED, MODES, TILE_SKIP, TILE_FULL, TILE_BOUNDARY,
     SVGA_OK, SVGA_EINVAL, SVGA_EUNSUPPORTED, SVGA_ECAPACITY, SVGA_EHIP,

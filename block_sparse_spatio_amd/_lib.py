@@ -44,6 +44,7 @@ SIGNATURES = {
     "svga_sparse_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, G, M, c_i32, c_f32, c_vp, c_vp,
                                      c_size, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "svga_attn_workspace_bytes": (c_i32, [ctypes.POINTER(c_size)]),
+    "svga_attn_split_workspace_bytes": (c_i32, [c_i32, c_i32, ctypes.POINTER(c_size)]),
     "svga_sparse_attn_fwd_ws": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, G, M, c_i32, c_f32, c_vp, c_vp,
                                         c_size, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),
 }

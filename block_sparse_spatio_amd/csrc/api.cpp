@@ -95,7 +95,7 @@ const char* svga_status_string(svga_status s) {
 
 const char* svga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t svga_version(void) { return 101; }
+int32_t svga_version(void) { return 102; }
 
 svga_status svga_tilemap_layout(const svga_geom* geom, int32_t bq, int32_t bkv, svga_tilemap_offsets* out) {
     TRY(check_geom(geom));
@@ -221,7 +221,7 @@ static svga_status attn_common(const char* who, const void* d_q, const void* d_k
                                float* d_lse, int32_t B, int32_t n_heads, const svga_geom* geom, const svga_mask* mask,
                                int32_t head_dim, float softmax_scale, const uint8_t* d_flags, const void* d_map,
                                size_t map_bytes, int32_t bq, int32_t bkv, int32_t mode, int32_t gather_temporal,
-                               int32_t* d_counter, void* stream) {
+                               int32_t* d_counter, int32_t split, void* stream) {
     TRY(check_geom(geom));
     TRY(check_mask(mask, geom));
     TRY(check_heads(B, n_heads));
@@ -261,6 +261,7 @@ static svga_status attn_common(const char* who, const void* d_q, const void* d_k
     a.gather = gather_temporal;
     a.scale = softmax_scale;
     a.counter = d_counter;
+    a.split = split;
     bool sup = true;
     (void)hipGetLastError();
     hipError_t e = launch_attn_fwd(a, static_cast<hipStream_t>(stream), &sup);
@@ -275,12 +276,20 @@ svga_status svga_sparse_attn_fwd(const void* d_q, const void* d_k, const void* d
                                  size_t map_bytes, int32_t bq, int32_t bkv, int32_t mode, int32_t gather_temporal,
                                  void* stream) {
     return attn_common("svga_sparse_attn_fwd", d_q, d_k, d_v, d_o, d_lse, B, n_heads, geom, mask, head_dim,
-                       softmax_scale, d_flags, d_map, map_bytes, bq, bkv, mode, gather_temporal, nullptr, stream);
+                       softmax_scale, d_flags, d_map, map_bytes, bq, bkv, mode, gather_temporal, nullptr, 0, stream);
 }
 
 svga_status svga_attn_workspace_bytes(size_t* bytes) {
     if (!bytes) return fail(SVGA_EINVAL, "bytes is NULL");
     *bytes = kAttnWorkspaceBytes;
+    return ok();
+}
+
+svga_status svga_attn_split_workspace_bytes(int32_t head_dim, int32_t bq, size_t* bytes) {
+    if (!bytes) return fail(SVGA_EINVAL, "bytes is NULL");
+    if (!attn_supported(head_dim, bq, 128))
+        return fail(SVGA_EUNSUPPORTED, "no attention kernel for head_dim=%d bq=%d", head_dim, bq);
+    *bytes = attn_split_workspace_bytes(head_dim, bq);
     return ok();
 }
 
@@ -292,10 +301,15 @@ svga_status svga_sparse_attn_fwd_ws(const void* d_q, const void* d_k, const void
     if (!d_workspace) return fail(SVGA_EINVAL, "d_workspace is NULL");
     if (workspace_bytes < kAttnWorkspaceBytes)
         return fail(SVGA_ECAPACITY, "workspace_bytes %zu < required %zu", workspace_bytes, kAttnWorkspaceBytes);
-    if (reinterpret_cast<uintptr_t>(d_workspace) % 4 != 0) return fail(SVGA_EINVAL, "d_workspace must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(d_workspace) % 16 != 0)
+        return fail(SVGA_EINVAL, "d_workspace must be 16-byte aligned");
+    const int32_t split = attn_supported(head_dim, bq, bkv) && bq >= 32 * kSplitWaves &&
+                                  workspace_bytes >= attn_split_workspace_bytes(head_dim, bq)
+                              ? 1
+                              : 0;
     return attn_common("svga_sparse_attn_fwd_ws", d_q, d_k, d_v, d_o, d_lse, B, n_heads, geom, mask, head_dim,
                        softmax_scale, d_flags, d_map, map_bytes, bq, bkv, mode, gather_temporal,
-                       static_cast<int32_t*>(d_workspace), stream);
+                       static_cast<int32_t*>(d_workspace), split, stream);
 }
 
 }  // extern "C"

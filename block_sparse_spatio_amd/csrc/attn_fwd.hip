@@ -45,6 +45,12 @@
 //   second loop that applies the exact mask (NAIVE / EXACT maps) or the
 //   padding mask (DENSE / ROUNDED maps). A row with no kept key so far keeps
 //   an exponent base of zero, so no NaN appears.
+// * Persistent launch (with a workspace): one workgroup per resident slot
+//   takes work items from a global counter. With the split-tail workspace
+//   the last items (one per resident 8-wave workgroup) run as kSplitParts
+//   pieces over contiguous shares of their key tile lists, each piece writing
+//   its normalised output and log-sum-exp, and merge_kernel combines them;
+//   the end of the launch then waits on a quarter of an item, not a whole one.
 // * Workgroups keep the hardware's round-robin spread over the 8 XCDs:
 //   every XCD gets every eighth query tile of every head, so the XCDs carry
 //   equal work. (Grouping consecutive query tiles on one XCD for L2 reuse
@@ -73,7 +79,16 @@ struct KArgs {
     int32_t exact;          // 1: exact mask on boundary tiles, 0: padding only
     int32_t qparts;         // workgroups per map query tile (its rows split in parts of this kernel's BQ)
     int32_t total;          // work items: BH * tq * qparts
-    int32_t* counter;       // persistent mode: next work item (zeroed before the launch); else null
+    int32_t* counter;       // persistent mode: next work unit (zeroed before the launch); else null
+    // Persistent mode with a split tail: items first_split .. total-1 run as
+    // kSplitParts pieces each, piece p taking the p-th contiguous share of the
+    // item's key tiles. Work units: the whole items below first_split, then
+    // the pieces, item by item.
+    int32_t units;          // first_split + (total - first_split) * kSplitParts
+    int32_t first_split;    // total when no item is split
+    int32_t split;          // 1: the workspace holds the split-tail region
+    float* part_lse;        // [kSplitItemsMax * kSplitParts][BQ] log-sum-exp of each piece's rows
+    uint16_t* part_o;       // [kSplitItemsMax * kSplitParts][BQ][D] normalised output of each piece (bf16)
     float c2;               // softmax_scale * log2(e)
     float scale;
 };
@@ -309,11 +324,21 @@ __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Four bf16 (round to nearest even) to p[0..3].
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float x0, float x1, float x2, float x3) {
+    uint2 w;
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x2) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x3) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+}
+
 // QB = 1: at most 256 registers per wave, so two waves share each SIMD (two
 // 4-wave workgroups, or one 8-wave workgroup, per CU).
-// One work item: the rows of (batch*head, query tile, part) `logical`.
+// One work item: the rows of (batch*head, query tile, part) `logical`. With
+// slot >= 0 the item is split: piece slot % kSplitParts of its key tiles
+// only, its state kept in piece slot `slot` (split item slot / kSplitParts).
 template <int D, int QB, int WAVES, int KSUB, bool GATHER>
-__device__ __forceinline__ void attn_item(const KArgs& a, const int logical, char* smem) {
+__device__ __forceinline__ void attn_item(const KArgs& a, const int logical, const int slot, char* smem) {
     constexpr bool PINGPONG = WAVES == 8 && QB == 1;
     constexpr int NT = WAVES * 64;
     constexpr int BQ = WAVES * QB * 32;
@@ -335,11 +360,23 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, cha
     // after barriers and LDS stores (a vector load there would put a full
     // memory latency in front of every step's K / V loads).
     typedef const __attribute__((address_space(4))) int32_t* ConstI32;
-    const ConstI32 kvl = (ConstI32)(a.kv + ((size_t)kind * a.tq + qt) * a.tk);
+    ConstI32 kvl = (ConstI32)(a.kv + ((size_t)kind * a.tq + qt) * a.tk);
     // list lengths and key-tile ids come from device memory: clamp them so
     // that no map content can send a load outside the K / V tensors
-    const int nf = imin(imax(a.n_full[kind * a.tq + qt], 0), a.tk);
-    const int ntiles = imin(nf + imax(a.n_bnd[kind * a.tq + qt], 0), a.tk);
+    int nf = imin(imax(a.n_full[kind * a.tq + qt], 0), a.tk);
+    int ntiles = imin(nf + imax(a.n_bnd[kind * a.tq + qt], 0), a.tk);
+    // Only the 8-wave ping-pong kernels run split items (kSplitWaves); in the
+    // others the piece code would cost the main loop registers.
+    constexpr bool SPLITS = WAVES == kSplitWaves && QB == 1;
+    if (SPLITS && slot >= 0) {
+        // a piece: the key tiles t0 .. t1-1 of the list
+        constexpr int P = (int)kSplitParts;
+        const int part = slot - (slot / P) * P;
+        const int t0 = ntiles * part / P, t1 = ntiles * (part + 1) / P;
+        kvl += t0;
+        nf = imin(imax(nf - t0, 0), t1 - t0);
+        ntiles = t1 - t0;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -547,33 +584,33 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, cha
         }
     }
 
-    // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = (base + log2 l) * ln 2
-    uint16_t* oh = a.o + head_off;
+    // ---- epilogue: O = acc / l, bf16 round-to-nearest-even; LSE = (base + log2 l) * ln 2.
+    // A piece of a split item writes both to its slot (rows relative to the
+    // item, LSE always) for merge_kernel.
+    const bool piece = SPLITS && slot >= 0;
+    constexpr int BQROWS = WAVES * QB * 32;
+    uint16_t* obase = piece ? a.part_o + (size_t)slot * BQROWS * D
+                            : a.o + head_off;
+    float* lbase = piece ? a.part_lse + (size_t)slot * BQROWS
+                         : (a.lse ? a.lse + (size_t)bh * N : nullptr);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lt = ws.lsum[qb] + __shfl_xor(ws.lsum[qb], 32);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const int row = row0 + (wave * QB + qb) * 32 + l32;
         if (row < N) {
-            const int orow = gat ? temporal_src(g, row) : row;
-            uint16_t* op = oh + (size_t)orow * D;
+            const int orow = piece ? row - row0 : (gat ? temporal_src(g, row) : row);
+            uint16_t* op = obase + (size_t)orow * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    __bf16 b0 = (__bf16)(ws.oacc[qb][db][4 * gq + 0] * inv);
-                    __bf16 b1 = (__bf16)(ws.oacc[qb][db][4 * gq + 1] * inv);
-                    __bf16 b2 = (__bf16)(ws.oacc[qb][db][4 * gq + 2] * inv);
-                    __bf16 b3 = (__bf16)(ws.oacc[qb][db][4 * gq + 3] * inv);
-                    uint2 w;
-                    w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-                    w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-                    *reinterpret_cast<uint2*>(op + db * 32 + 8 * gq + 4 * h) = w;
-                }
+                for (int gq = 0; gq < 4; ++gq)
+                    store_bf16x4(op + db * 32 + 8 * gq + 4 * h, ws.oacc[qb][db][4 * gq] * inv,
+                                 ws.oacc[qb][db][4 * gq + 1] * inv, ws.oacc[qb][db][4 * gq + 2] * inv,
+                                 ws.oacc[qb][db][4 * gq + 3] * inv);
             }
-            if (a.lse && h == 0)
-                a.lse[(size_t)bh * N + orow] =
-                    lt > 0.f ? (ws.base[qb] + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
+            if (lbase && h == 0)
+                lbase[orow] = lt > 0.f ? (ws.base[qb] + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
         }
     }
 }
@@ -590,7 +627,7 @@ void attn_fwd_kernel(KArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[(PINGPONG ? 4 : 2) * St::STAGE];
     __shared__ int next;
     if (!a.counter) {
-        attn_item<D, QB, WAVES, KSUB, GATHER>(a, blockIdx.x, smem);
+        attn_item<D, QB, WAVES, KSUB, GATHER>(a, blockIdx.x, -1, smem);
         return;
     }
     for (;;) {
@@ -598,8 +635,11 @@ void attn_fwd_kernel(KArgs a) {
         __syncthreads();
         const int t = next;
         __syncthreads();   // every wave has read `next` before it changes; the last item's LDS reads are done
-        if (t >= a.total) break;
-        attn_item<D, QB, WAVES, KSUB, GATHER>(a, t, smem);
+        if (t >= a.units) break;
+        // unit u past first_split is piece slot u: item first_split + u / kSplitParts
+        const int slot = t >= a.first_split ? t - a.first_split : -1;
+        const int logical = slot >= 0 ? a.first_split + slot / (int)kSplitParts : t;
+        attn_item<D, QB, WAVES, KSUB, GATHER>(a, logical, slot, smem);
     }
 }
 
@@ -607,8 +647,71 @@ __global__ void zero_counter_kernel(int32_t* c) {
     if (threadIdx.x == 0) *c = 0;
 }
 
+// Merge of the split items' pieces (ASTA section "Avoid intra-tile masking
+// when there is nothing to mask": partial results over disjoint key sets
+// combine through their softmax statistics). Piece p of a row holds its
+// normalised output O_p and log-sum-exp L_p; with m = max_p L_p and
+// w_p = e^(L_p - m): O = sum_p w_p O_p / sum_p w_p, LSE = m + ln sum_p w_p.
+// A piece that kept no key of the row has L_p = -inf and weight 0. One
+// thread per 8 dims of one row; `rows` = query rows of one work item.
+template <int D, bool GATHER>
+__global__ __launch_bounds__(256) void merge_kernel(KArgs a, int rows) {
+    constexpr int CH = D / 8;
+    constexpr int P = (int)kSplitParts;
+    const int gid = blockIdx.x * 256 + threadIdx.x;
+    const int item = gid / (rows * CH);
+    if (item >= a.total - a.first_split) return;
+    const int rem = gid - item * rows * CH;
+    const int r = rem / CH, c = rem - r * CH;
+    const int logical = a.first_split + item;
+    const int N = a.g.N;
+    const int per_bh = a.tq * a.qparts;
+    const int bh = logical / per_bh;
+    const int qrem = logical - bh * per_bh;
+    const int qt = qrem / a.qparts;
+    const int row = qt * rows * a.qparts + (qrem - qt * a.qparts) * rows + r;
+    if (row >= N) return;
+    const size_t slot0 = (size_t)item * P;
+    const float* part_lse = a.part_lse;
+    const uint16_t* part_o = a.part_o;
+    float lp[P];
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        lp[p] = part_lse[(slot0 + p) * rows + r];
+        m = fmaxf(m, lp[p]);
+    }
+    float w[P];
+    float wsum = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        w[p] = lp[p] > -INFINITY ? __builtin_amdgcn_exp2f((lp[p] - m) * 1.4426950408889634f) : 0.f;
+        wsum += w[p];
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint4 x = *reinterpret_cast<const uint4*>(part_o + ((slot0 + p) * rows + r) * D + 8 * c);
+        const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w[p] * __builtin_bit_cast(float, u[e] << 16);
+            acc[2 * e + 1] += w[p] * __builtin_bit_cast(float, u[e] & 0xffff0000u);
+        }
+    }
+    const int orow = GATHER && a.flags[bh] ? temporal_src(a.g, row) : row;
+    uint16_t* op = a.o + ((size_t)bh * N + orow) * D + 8 * c;
+    store_bf16x4(op, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    store_bf16x4(op + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (a.lse && c == 0) a.lse[(size_t)bh * N + orow] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 template <int D, int QB, int WAVES, int KSUB>
-hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
+hipError_t launch_one(const KArgs& k0, bool gather, hipStream_t stream) {
+    KArgs k = k0;
+    k.units = k.total;
+    k.first_split = k.total;
     unsigned nwg = (unsigned)k.total;
     if (k.counter) {
         // as many workgroups as can be resident at once
@@ -621,7 +724,13 @@ hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(
                              &per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, false>, WAVES * 64, 0);
         if (e != hipSuccess) return e;
-        nwg = (unsigned)imin(k.total, cus * imax(per_cu, 1));
+        const int resident = cus * imax(per_cu, 1);
+        // split tail: the last min(resident, total) items (at most the
+        // workspace's capacity) run in pieces
+        const int nsplit = k.split && WAVES == kSplitWaves && QB == 1 ? imin(imin(resident, k.total), (int)kSplitItemsMax) : 0;
+        k.first_split = k.total - nsplit;
+        k.units = k.first_split + nsplit * (int)kSplitParts;
+        nwg = (unsigned)imin(k.units, resident);
         hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, stream, k.counter);
     }
     if (nwg == 0) return hipGetLastError();
@@ -630,6 +739,16 @@ hipError_t launch_one(const KArgs& k, bool gather, hipStream_t stream) {
         hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, true>), grid, dim3(WAVES * 64), 0, stream, k);
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, QB, WAVES, KSUB, false>), grid, dim3(WAVES * 64), 0, stream, k);
+    const int nsplit = k.total - k.first_split;
+    if (nsplit > 0) {
+        constexpr int ROWS = WAVES * QB * 32;
+        const unsigned threads = (unsigned)nsplit * ROWS * (D / 8);
+        const dim3 mgrid((threads + 255) / 256);
+        if (gather)
+            hipLaunchKernelGGL((merge_kernel<D, true>), mgrid, dim3(256), 0, stream, k, ROWS);
+        else
+            hipLaunchKernelGGL((merge_kernel<D, false>), mgrid, dim3(256), 0, stream, k, ROWS);
+    }
     return hipGetLastError();
 }
 
@@ -697,6 +816,14 @@ hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* suppor
     k.qparts = 1;
     k.total = a.BH * a.L.tq;
     k.counter = a.counter;
+    k.split = a.counter && a.split ? 1 : 0;
+    k.part_lse = nullptr;
+    k.part_o = nullptr;
+    if (k.split) {
+        char* base = reinterpret_cast<char*>(a.counter);
+        k.part_lse = reinterpret_cast<float*>(base + kSplitLseOffset);
+        k.part_o = reinterpret_cast<uint16_t*>(base + kSplitLseOffset + split_lse_bytes(a.bq));
+    }
     k.c2 = a.scale * 1.4426950408889634f;
     k.scale = a.scale;
     const int ksub = a.bkv % 64 == 0 ? 64 : 32;

@@ -239,9 +239,24 @@ struct AttnLaunch {
     int32_t head_dim, bq, bkv, mode, gather;
     float scale;
     int32_t* counter;      // persistent workgroups: work counter in the caller's workspace, or null
+    int32_t split;         // 1: the workspace also holds the split-tail region (attn_split_workspace_bytes)
 };
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* supported);
 constexpr size_t kAttnWorkspaceBytes = 256;   // the work counter, padded
+// Split tail of the persistent launch (kernels of kSplitWaves waves, bq 256
+// and 512): at most kSplitItemsMax items, kSplitParts pieces each. Workspace layout: counter at 0; log-sum-exp [items * parts][rows]
+// (fp32) at kSplitLseOffset; then the normalised output pieces [items * parts]
+// [rows][head_dim] (bf16). rows = the query rows of one workgroup, min(bq, 256).
+constexpr int kSplitWaves = 8;
+constexpr size_t kSplitItemsMax = 256;
+constexpr size_t kSplitParts = 4;
+constexpr size_t kSplitLseOffset = 256;
+inline size_t split_rows(int32_t bq) { return bq > 256 ? 256 : (size_t)bq; }
+inline size_t split_lse_bytes(int32_t bq) { return kSplitItemsMax * kSplitParts * split_rows(bq) * 4; }
+inline size_t attn_split_workspace_bytes(int32_t head_dim, int32_t bq) {
+    if (bq < 32 * kSplitWaves) return kAttnWorkspaceBytes;   // no split below 256-row workgroups
+    return kSplitLseOffset + split_lse_bytes(bq) + kSplitItemsMax * kSplitParts * split_rows(bq) * head_dim * 2;
+}
 bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv);
 
 hipError_t launch_permute(const void* in, void* out, const uint8_t* flags, int32_t BH, const Geo& g,

@@ -181,11 +181,20 @@ def svga_attn_workspace_bytes():
     return n.value
 
 
+def svga_attn_split_workspace_bytes(head_dim, bq):
+    """Device workspace bytes with which svga_sparse_attn_fwd_ws also splits its last query tiles."""
+    n = ctypes.c_size_t()
+    _check(lib().svga_attn_split_workspace_bytes(int(head_dim), int(bq), ctypes.byref(n)))
+    return n.value
+
+
 def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, softmax_scale=None,
                          gather_temporal=False, out=None, lse=None, want_lse=False, workspace=None, stream=None):
     """Block-sparse attention forward. Returns (out, lse); lse is None unless requested.
-    With `workspace` (a device tensor of at least svga_attn_workspace_bytes() bytes) the call runs
-    persistent workgroups (svga_sparse_attn_fwd_ws); the results are the same bits."""
+    With `workspace` (a 16-byte aligned device tensor of at least svga_attn_workspace_bytes() bytes)
+    the call runs persistent workgroups (svga_sparse_attn_fwd_ws): the same bits as without it, unless
+    the workspace holds svga_attn_split_workspace_bytes(d, bq) bytes, in which case the last query
+    tiles run in pieces merged through their softmax statistics (equal up to rounding)."""
     _qkv_check(q, k, v)
     B, H, N, d = q.shape
     out = torch.empty_like(q) if out is None else out

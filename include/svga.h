@@ -227,17 +227,38 @@ svga_status svga_sparse_attn_fwd(const void* d_q, const void* d_k, const void* d
 /* Device workspace bytes that svga_sparse_attn_fwd_ws needs (a work counter). */
 svga_status svga_attn_workspace_bytes(size_t* bytes);
 
+/* Device workspace bytes with which svga_sparse_attn_fwd_ws also splits the
+ * tail of its work (ASTA section "Avoid intra-tile masking when there is
+ * nothing to mask": partial results over disjoint key sets combine through
+ * their softmax statistics). For bq 256 and 512: the last query tiles (256-row
+ * parts of a 512-row tile), as many as the device holds workgroups at once
+ * and at most 256, each run as 4 pieces over contiguous quarters of their key
+ * tile lists; each piece stores its normalised output O_p (bf16) and its
+ * log-sum-exp L_p in the workspace, and a second kernel on the same stream
+ * writes, with m = max_p L_p and w_p = e^(L_p - m),
+ * O = sum_p w_p O_p / sum_p w_p and LSE = m + ln sum_p w_p. About 68 MB at
+ * head_dim 128. Smaller bq do not split: svga_attn_workspace_bytes' size.
+ * Depends on head_dim and bq only.
+ * SVGA_EUNSUPPORTED for a head_dim / bq without an attention kernel,
+ * SVGA_EINVAL if bytes is NULL. */
+svga_status svga_attn_split_workspace_bytes(int32_t head_dim, int32_t bq, size_t* bytes);
+
 /* The operation of svga_sparse_attn_fwd (ASTA section "Logical sparsity is
  * not physical sparsity": the tile walk over each query tile's FULL, then
  * BOUNDARY key tiles), launched as persistent workgroups: as many workgroups
  * as the device holds at once, each taking the next (batch, head, query tile) from a
  * counter in d_workspace until none is left (no workgroup launch between
  * query tiles, and no CU idles while the in-order dispatcher waits on a busy
- * one). Same arguments, same results bit for bit, plus:
+ * one). Same arguments, plus:
  * d_workspace: caller-owned device memory, at least svga_attn_workspace_bytes
- *   bytes, 4-byte aligned; its content on entry does not matter (the call
- *   clears it on the stream first) and is undefined afterwards.
+ *   bytes, 16-byte aligned; its content on entry does not matter (the call
+ *   clears what it needs on the stream first) and is undefined afterwards.
  *   SVGA_EINVAL if NULL or misaligned, SVGA_ECAPACITY if too small.
+ * Below svga_attn_split_workspace_bytes(head_dim, bq) bytes, and for bq
+ * below 256, the results are those of svga_sparse_attn_fwd bit for bit; from
+ * there on the last query tiles run split (see
+ * svga_attn_split_workspace_bytes) and their rows equal svga_sparse_attn_fwd's
+ * up to the bf16 rounding of the pieces' outputs.
  * Calls that share one workspace must not overlap (one stream, or ordered). */
 svga_status svga_sparse_attn_fwd_ws(const void* d_q, const void* d_k, const void* d_v,
                                     void* d_o, float* d_lse,

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == len(_lib.SIGNATURES) == 13
+    assert len(names) == len(_lib.SIGNATURES) == 14
     assert set(names) == set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(L, n), n
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.svga_version() == 101
+    assert L.svga_version() == 102
     assert L.svga_status_string(0) == b"ok"
     assert L.svga_status_string(-3) == b"buffer too small"
 
@@ -108,6 +108,17 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.svga_sparse_attn_fwd_ws(*common, None, n.value, None) == -1
     assert L.svga_sparse_attn_fwd_ws(*common, FAKE, n.value - 1, None) == -3
     assert L.svga_sparse_attn_fwd_ws(*common, ctypes.c_void_p(0x1002), n.value, None) == -1
+    assert L.svga_sparse_attn_fwd_ws(*common, ctypes.c_void_p(0x1008), n.value, None) == -1
+    # split-tail workspace: only 256-row workgroups split; it grows with head_dim
+    s = {}
+    for d, bq in ((64, 32), (64, 256), (128, 128), (128, 256), (128, 512)):
+        assert L.svga_attn_split_workspace_bytes(d, bq, ctypes.byref(n)) == 0
+        s[d, bq] = n.value
+    assert s[128, 256] == s[128, 512] > s[64, 256] > s[128, 128] == s[64, 32] == 256
+    assert s[128, 256] == 256 + 256 * 4 * 256 * (4 + 128 * 2)
+    assert L.svga_attn_split_workspace_bytes(96, 256, ctypes.byref(n)) == -2
+    assert L.svga_attn_split_workspace_bytes(128, 48, ctypes.byref(n)) == -2
+    assert L.svga_attn_split_workspace_bytes(128, 256, None) == -1
     bad = (*a, o, None, 1, 2, g, m, 96, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, 32, 32, 2, 0)
     assert L.svga_sparse_attn_fwd_ws(*bad, FAKE, n.value, None) == -2
 

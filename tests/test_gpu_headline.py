@@ -187,6 +187,39 @@ def test_headline_persistent_equals_plain_bitwise(dev, headline):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+def test_headline_split_tail(dev, headline):
+    """The benchmark's launch with the split-tail workspace: the last 256 query tiles (head 9's tiles
+    40-295) run as 4 merged pieces each. Against the unsplit launch on every row, and against the
+    oracle on sampled rows of those tiles."""
+    w, q, k, v, qd, kd, vd = headline
+    geom, mask = geom_mask(w)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say("headline split tail")
+    tm = B.svga_build_tilemap(geom, mask, 256, 128, B.MAP_EXACT, device=dev)
+    qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (qd, kd, vd))
+    ws = torch.zeros(B.svga_attn_split_workspace_bytes(w.d, 256), dtype=torch.uint8, device=dev)
+    a, la = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, 256, 128, B.MAP_EXACT, want_lse=True)
+    b, lb = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, 256, 128, B.MAP_EXACT, want_lse=True,
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    d = (a.float() - b.float()).abs()
+    say(f"  split vs unsplit: max-abs {d.max().item():.3e}; rows differing only in head 9 from row 10240")
+    assert torch.equal(a[0, :9].view(torch.int16), b[0, :9].view(torch.int16))
+    assert torch.equal(a[0, 9, :40 * 256].view(torch.int16), b[0, 9, :40 * 256].view(torch.int16))
+    assert d.max().item() < 1e-2 and (la - lb).abs().max().item() < 1e-4
+    o = B.svga_unpermute(b, flags, geom, mask).cpu()
+    h = 9
+    order = O.executed_order(w.F, w.H, w.W, w.kinds[h], mask[0], mask[3])
+    pick = np.random.default_rng(9).choice(np.arange(40 * 256, w.N), 96, replace=False)
+    rows = np.unique(np.concatenate([order[pick], order[-32:]]))
+    ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                              w.kinds[h], w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, 256, 128,
+                              1 / math.sqrt(w.d), rows=rows)
+    err = np.abs(o[0, h, rows].double().numpy() - ref)
+    say(f"  head {h}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
 def test_1440p_routing_and_attention(dev):
     """Routing on 64 sampled queries at 302,400 tokens finds the planted head kinds; the routed
     pipeline matches the oracle on sampled rows."""

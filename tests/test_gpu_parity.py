@@ -202,6 +202,58 @@ def test_persistent_equals_plain_bitwise(dev, tiles, mode, gather):
         assert torch.equal(la.view(torch.int32), lb.view(torch.int32))
 
 
+@pytest.mark.parametrize("wname,tiles,mode,gather", [
+    ("small", (256, 128), 2, False), ("small", (256, 128), 3, True), ("small", (512, 128), 2, False),
+    ("small", (128, 64), 0, False), ("small", (256, 512), 2, False), ("small", (256, 96), 1, True),
+    ("tiny", (32, 32), 2, False), ("tiny", (64, 32), 1, True)])
+def test_split_tail(dev, wname, tiles, mode, gather):
+    """Persistent launch with the split-tail workspace: at bq 256 / 512 every work item here is among
+    the last ones, so each runs as 4 pieces merged through their log-sum-exp (pieces with no key tile
+    included at 512-key tiles); smaller bq do not split and must give the unsplit bits. Against the
+    oracle on every row of two heads, and against the unsplit launch on every row (output to bf16
+    rounding, LSE to fp32 rounding); the workspace starts as garbage and is reused by a second,
+    smaller call."""
+    w = SMALL if wname == "small" else TINY
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    bq, bkv = tiles
+    say(f"split tail {wname} tiles={tiles} mode={mode} gather={gather}")
+    qc, kc, vc = normal_qkv(2, w.heads, w.N, w.d, seed=6)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    flags = torch.tensor([list(w.kinds)] * 2, dtype=torch.uint8, device=dev)
+    tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
+    ws = torch.full((B.svga_attn_split_workspace_bytes(w.d, bq),), 0x5A, dtype=torch.uint8, device=dev)
+    scale = 1 / math.sqrt(w.d)
+    for batch in (2, 1):
+        fb = flags[:batch]
+        if gather:
+            qb, kb, vb = q[:batch], k[:batch], v[:batch]
+        else:
+            qb, kb, vb = (B.svga_permute(x[:batch].contiguous(), fb, geom, mask) for x in (q, k, v))
+        a, la = B.svga_sparse_attn_fwd(qb, kb, vb, fb, tm, geom, mask, bq, bkv, mode, gather_temporal=gather,
+                                       want_lse=True)
+        b, lb = B.svga_sparse_attn_fwd(qb, kb, vb, fb, tm, geom, mask, bq, bkv, mode, gather_temporal=gather,
+                                       want_lse=True, workspace=ws)
+        if not gather:
+            b = B.svga_unpermute(b, fb, geom, mask)
+            a = B.svga_unpermute(a, fb, geom, mask)
+        torch.cuda.synchronize()
+        d = (a.float() - b.float()).abs()
+        say(f"  batch {batch}: split vs unsplit max-abs {d.max().item():.3e} mean-abs {d.mean().item():.3e}")
+        if bq < 256:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+        assert torch.isfinite(b.float()).all()
+        assert d.max().item() < 1e-2 and d.mean().item() < 5e-4
+        fin = torch.isfinite(la)
+        assert torch.equal(fin, torch.isfinite(lb))
+        assert (la[fin] - lb[fin]).abs().max().item() < 1e-4
+        bc = b.cpu()
+        for h in (0, w.heads - 1):
+            ref, _ = oracle_head(geom, mask, qc[batch - 1, h], kc[batch - 1, h], vc[batch - 1, h], w.kinds[h], mode,
+                                 bq, bkv, scale)
+            assert_close(bc[batch - 1, h].float().numpy(), ref, f"head {h}")
+
+
 def test_gather_equals_permute_path_bitwise(dev):
     """In-kernel gather of temporal rows gives the same bits as permute -> attention -> unpermute."""
     w = SMALL
