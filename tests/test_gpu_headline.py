@@ -48,14 +48,15 @@ def headline(dev):
     return w, q, k, v, q.to(dev), k.to(dev), v.to(dev)
 
 
-def pipeline(dev, w, qd, kd, vd, flags, bq, bkv, mode, gather=False):
+def pipeline(dev, w, qd, kd, vd, flags, bq, bkv, mode, gather=False, workspace=None):
     geom, mask = geom_mask(w)
     tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
     if gather:
-        o, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, bq, bkv, mode, gather_temporal=True)
+        o, _ = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, bq, bkv, mode, gather_temporal=True,
+                                      workspace=workspace)
         return o
     qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (qd, kd, vd))
-    op, _ = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode)
+    op, _ = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode, workspace=workspace)
     return B.svga_unpermute(op, flags, geom, mask)
 
 
@@ -242,10 +243,21 @@ def test_1440p_routing_and_attention(dev):
         assert np.abs(e[0, h] - er[0, 0]).max() <= 1e-3 * er[0, 0].max()
         assert f[0, h] == fr[0, 0]
     assert tuple(f[0]) == w.kinds
-    say("1440p attention")
-    o = pipeline(dev, w, qd, kd, vd, flags, w.bq, w.bkv, B.MAP_EXACT).cpu()
-    for h in (1, 8):
-        rows = sample_rows(w.N, w.bq, 32, seed=30 + h)
+    say("1440p attention (split-tail launch, as timed) and plain launch")
+    ws = torch.empty(B.svga_attn_split_workspace_bytes(w.d, w.bq), dtype=torch.uint8, device=dev)
+    o = pipeline(dev, w, qd, kd, vd, flags, w.bq, w.bkv, B.MAP_EXACT, workspace=ws)
+    plain = pipeline(dev, w, qd, kd, vd, flags, w.bq, w.bkv, B.MAP_EXACT)
+    d = (o.float() - plain.float()).abs()
+    say(f"  split vs plain: max-abs {d.max().item():.3e} mean-abs {d.mean().item():.3e}")
+    assert d.max().item() < 1e-2
+    assert torch.equal(o[0, :9].view(torch.int16), plain[0, :9].view(torch.int16))
+    o = o.cpu()
+    # head 9 (temporal): its last 256 query tiles are the split ones
+    order9 = O.executed_order(w.F, w.H, w.W, w.kinds[9], mask[0], mask[3])
+    tq = -(-w.N // w.bq)
+    split_rows = order9[np.random.default_rng(39).choice(np.arange((tq - 256) * w.bq, w.N), 32, replace=False)]
+    for h in (1, 8, 9):
+        rows = sample_rows(w.N, w.bq, 32, seed=30 + h) if h != 9 else np.unique(split_rows)
         ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
                                   w.kinds[h], w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, w.bq, w.bkv, scale,
                                   rows=rows)
