@@ -72,8 +72,24 @@ def _stream(stream):
 
 def _qkv_check(*ts):
     for t in ts:
-        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous() and t.dim() == 4):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()
+                and t.dim() == 4):
             raise ValueError("expected contiguous bfloat16 CUDA tensors of shape [B, heads, N, head_dim]")
+        if t.shape != ts[0].shape or t.device != ts[0].device:
+            raise ValueError(f"tensor of shape {tuple(t.shape)} on {t.device} does not match "
+                             f"{tuple(ts[0].shape)} on {ts[0].device}")
+
+
+def _buf(name, t, device, dtype=None, min_numel=0):
+    """A device buffer handed to the library: contiguous, on `device`, of `dtype`, large enough."""
+    if t is None:
+        return
+    if not (isinstance(t, torch.Tensor) and t.device == device and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {min_numel}")
 
 
 def svga_version():
@@ -100,6 +116,9 @@ def svga_build_tilemap(geom, mask, bq, bkv, mode, out=None, device="cuda", strea
     off = svga_tilemap_layout(geom, bq, bkv)
     if out is None:
         out = torch.empty(off.total, dtype=torch.uint8, device=device)
+    if not (isinstance(out, torch.Tensor) and out.is_cuda):
+        raise ValueError("out must be a CUDA tensor")
+    _buf("out", out, out.device, torch.uint8)
     _check(lib().svga_build_tilemap(ctypes.byref(_geom(geom)), ctypes.byref(_mask(mask)), int(bq), int(bkv),
                                     _mode(mode), _vp(out), out.numel() * out.element_size(), _stream(stream)))
     return out
@@ -130,8 +149,9 @@ def tilemap_views(blob, geom, bq, bkv):
 def _permute(fn, x, flags, geom, mask, out, stream):
     _qkv_check(x)
     out = torch.empty_like(x) if out is None else out
-    _qkv_check(out)
+    _qkv_check(x, out)
     B, H, N, d = x.shape
+    _buf("flags", flags, x.device, torch.uint8, B * H)
     _check(fn(_vp(x), _vp(out), _vp(flags), B, H, ctypes.byref(_geom(geom)), ctypes.byref(_mask(mask)), d,
               _stream(stream)))
     return out
@@ -166,6 +186,10 @@ def svga_route_heads(q, k, v, geom, mask, sample_idx, softmax_scale=None, worksp
         flags_out = torch.empty(B, H, dtype=torch.uint8, device=q.device)
     if err_out is None and want_err:
         err_out = torch.empty(B, H, 2, dtype=torch.float32, device=q.device)
+    _buf("sample_idx", sample_idx, q.device, torch.int32)
+    _buf("workspace", workspace, q.device)
+    _buf("flags_out", flags_out, q.device, torch.uint8, B * H)
+    _buf("err_out", err_out, q.device, torch.float32, B * H * 2)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     _check(lib().svga_route_heads(_vp(q), _vp(k), _vp(v), B, H, ctypes.byref(_geom(geom)),
                                   ctypes.byref(_mask(mask)), d, _vp(sample_idx), ns, float(scale), _vp(workspace),
@@ -198,9 +222,13 @@ def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, sof
     _qkv_check(q, k, v)
     B, H, N, d = q.shape
     out = torch.empty_like(q) if out is None else out
-    _qkv_check(out)
+    _qkv_check(q, out)
     if lse is None and want_lse:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    _buf("lse", lse, q.device, torch.float32, B * H * N)
+    _buf("flags", flags, q.device, torch.uint8, B * H)
+    _buf("tilemap", tilemap, q.device, torch.uint8)
+    _buf("workspace", workspace, q.device)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     args = (_vp(q), _vp(k), _vp(v), _vp(out), _vp(lse), B, H, ctypes.byref(_geom(geom)), ctypes.byref(_mask(mask)), d,
             float(scale), _vp(flags), _vp(tilemap), tilemap.numel() * tilemap.element_size(), int(bq), int(bkv),

@@ -254,6 +254,36 @@ def test_split_tail(dev, wname, tiles, mode, gather):
             assert_close(bc[batch - 1, h].float().numpy(), ref, f"head {h}")
 
 
+def test_binding_rejects_bad_buffers(dev):
+    """The binding refuses host tensors, short buffers and mismatched shapes before anything is
+    launched (a host pointer or a short buffer handed to a kernel would be read out of bounds)."""
+    w = TINY
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    q = torch.zeros(1, 2, w.N, w.d, dtype=torch.bfloat16, device=dev)
+    flags = torch.zeros(1, 2, dtype=torch.uint8, device=dev)
+    tm = B.svga_build_tilemap(geom, mask, 32, 32, "exact", device=dev)
+    attn = lambda **kw: B.svga_sparse_attn_fwd(kw.pop("q", q), kw.pop("k", q), q, kw.pop("flags", flags),
+                                               kw.pop("tm", tm), geom, mask, 32, 32, "exact", **kw)
+    bad = [dict(k=q[:, :, :96].contiguous()), dict(k=q.cpu()), dict(flags=flags.cpu()), dict(flags=flags[:, :1]),
+           dict(tm=tm.cpu()), dict(tm=tm.to(torch.int32)), dict(workspace=torch.empty(256, dtype=torch.uint8)),
+           dict(lse=torch.empty(1, dtype=torch.float32, device=dev)), dict(out=q[:, :1].contiguous())]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            attn(**kw)
+    with pytest.raises(ValueError):
+        B.svga_permute(q, flags[:, :1].contiguous(), geom, mask)
+    with pytest.raises(ValueError):
+        B.svga_route_heads(q, q, q, geom, mask, torch.arange(4, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        B.svga_route_heads(q, q, q, geom, mask, torch.arange(4, dtype=torch.int64, device=dev))
+    with pytest.raises(ValueError):
+        B.svga_build_tilemap(geom, mask, 32, 32, "exact", out=torch.empty(tm.numel(), dtype=torch.uint8))
+    o, _ = attn()   # the same call with good buffers runs
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_gather_equals_permute_path_bitwise(dev):
     """In-kernel gather of temporal rows gives the same bits as permute -> attention -> unpermute."""
     w = SMALL
