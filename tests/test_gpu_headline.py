@@ -221,6 +221,33 @@ def test_headline_split_tail(dev, headline):
     assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
 
 
+def test_headline_whole_query_tiles(dev, headline):
+    """Every row of the first and last query tiles and of the two query tiles with the most
+    BOUNDARY key tiles, for one spatial and one temporal head, in the benchmark's launch (split
+    tail included: head 9's last tiles are split)."""
+    w, q, k, v, qd, kd, vd = headline
+    geom, mask = geom_mask(w)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.svga_attn_split_workspace_bytes(w.d, 256), dtype=torch.uint8, device=dev)
+    say("headline whole query tiles")
+    o = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT, workspace=ws).cpu()
+    hv = B.tilemap_views(B.svga_build_tilemap_host(geom, mask, 256, 128, B.MAP_EXACT), geom, 256, 128)
+    for h in (0, 9):
+        kind = w.kinds[h]
+        nb = hv["n_bnd"][kind]
+        tiles = sorted({0, nb.size - 1, *[int(t) for t in np.argsort(-nb, kind="stable")[:2]]})
+        order = O.executed_order(w.F, w.H, w.W, kind, mask[0], mask[3])
+        rows = np.concatenate([order[t * 256:min(w.N, (t + 1) * 256)] for t in tiles])
+        ref, _ = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                                  kind, w.F, w.H, w.W, *mask[:3], mask[3], O.MODE_EXACT, 256, 128,
+                                  1 / math.sqrt(w.d), rows=rows)
+        err = np.abs(o[0, h, rows].double().numpy() - ref)
+        say(f"  head {h}: query tiles {tiles} (boundary key tiles {[int(nb[t]) for t in tiles]}), "
+            f"{rows.size} rows: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+        assert np.isfinite(o[0, h, rows].float().numpy()).all()
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+
+
 def test_1440p_routing_and_attention(dev):
     """Routing on 64 sampled queries at 302,400 tokens finds the planted head kinds; the routed
     pipeline matches the oracle on sampled rows."""
