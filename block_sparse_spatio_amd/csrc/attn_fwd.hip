@@ -636,10 +636,14 @@ void attn_fwd_kernel(KArgs a) {
         const int t = next;
         __syncthreads();   // every wave has read `next` before it changes; the last item's LDS reads are done
         if (t >= a.units) break;
-        // unit u past first_split is piece slot u: item first_split + u / kSplitParts
-        const int slot = t >= a.first_split ? t - a.first_split : -1;
-        const int logical = slot >= 0 ? a.first_split + slot / (int)kSplitParts : t;
-        attn_item<D, QB, WAVES, KSUB, GATHER>(a, logical, slot, smem);
+        if constexpr (WAVES == kSplitWaves && QB == 1) {
+            // unit u past first_split is piece slot u: item first_split + u / kSplitParts
+            const int slot = t >= a.first_split ? t - a.first_split : -1;
+            const int logical = slot >= 0 ? a.first_split + slot / (int)kSplitParts : t;
+            attn_item<D, QB, WAVES, KSUB, GATHER>(a, logical, slot, smem);
+        } else {
+            attn_item<D, QB, WAVES, KSUB, GATHER>(a, t, -1, smem);   // no split items here
+        }
     }
 }
 
