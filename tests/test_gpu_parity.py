@@ -4,6 +4,7 @@ Bars: tile maps and permutations bit-exact; bf16 attention outputs within
 max-abs 2e-2 and mean-abs 2e-3 of the fp64 oracle (plus exact-rational census
 checks); routing errors within 1e-3 relative, flags equal except near-ties.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -205,7 +206,8 @@ def test_persistent_equals_plain_bitwise(dev, tiles, mode, gather):
 @pytest.mark.parametrize("wname,tiles,mode,gather", [
     ("small", (256, 128), 2, False), ("small", (256, 128), 3, True), ("small", (512, 128), 2, False),
     ("small", (128, 64), 0, False), ("small", (256, 512), 2, False), ("small", (256, 96), 1, True),
-    ("tiny", (32, 32), 2, False), ("tiny", (64, 32), 1, True)])
+    ("tiny", (32, 32), 2, False), ("tiny", (64, 32), 1, True),
+    ("small64", (256, 128), 2, False), ("small64", (512, 64), 3, True)])
 def test_split_tail(dev, wname, tiles, mode, gather):
     """Persistent launch with the split-tail workspace: at bq 256 / 512 every work item here is among
     the last ones, so each runs as 4 pieces merged through their log-sum-exp (pieces with no key tile
@@ -213,7 +215,7 @@ def test_split_tail(dev, wname, tiles, mode, gather):
     oracle on every row of two heads, and against the unsplit launch on every row (output to bf16
     rounding, LSE to fp32 rounding); the workspace starts as garbage and is reused by a second,
     smaller call."""
-    w = SMALL if wname == "small" else TINY
+    w = {"small": SMALL, "tiny": TINY, "small64": dataclasses.replace(SMALL, d=64)}[wname]
     geom = (w.F, w.H, w.W)
     mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
     bq, bkv = tiles
