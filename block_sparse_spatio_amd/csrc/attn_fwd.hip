@@ -487,10 +487,23 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
+        // gathered rows: the source rows of the keys that step s's transfer loads,
+        // found in the matrix phase before it (where VALU time is free): lane i
+        // finds the source of key kb + i, each chunk takes its row's from that lane
+        int srow[Sh::CU];
+        auto prep = [&](int s) __attribute__((always_inline)) {
+            if constexpr (GATHER) {
+                const int my = next_keys(s) + lane;
+                const int mysrc = lane < KSUB && my < N ? (gat ? temporal_src(g, my) : my) : -1;
+#pragma unroll
+                for (int r = 0; r < Sh::CU; ++r) srow[r] = __shfl(mysrc, Sh::chunk_row(r, htid));
+            }
+        };
         // softmax of step t; with XFER (waves 4-7, step s) the stage transfer rides along
         auto soft = [&](auto masked, auto xfer, int t, int s) __attribute__((always_inline)) {
             char* dst = wstage(s + 1);
             const int kb = decltype(xfer)::value ? next_keys(s) : 0;
+
             // chunk r goes with hook point r * NH / CU (NH = KSUB / 16 points)
             auto hook = [&](int k) __attribute__((always_inline)) {
                 if constexpr (decltype(xfer)::value) {
@@ -500,7 +513,10 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
                         if (r * NH / Sh::CU != k) continue;
                         __builtin_amdgcn_sched_barrier(0);
                         sh.store_chunk(r, dst, htid);
-                        sh.load_chunk(r, rsk, rsv, kb, N, src, htid);
+                        if constexpr (GATHER)
+                            sh.load_chunk_at(r, rsk, rsv, srow[r], htid);
+                        else
+                            sh.load_chunk(r, rsk, rsv, kb, N, src, htid);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -563,18 +579,21 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
             sh.load(kh, vh, next_keys(0), N, src, htid);
             phase_barrier();
             prod(One{}, 0);
+            prep(1);
             int s = 1;
             for (; s < imin(sf + 1, steps); ++s) {
                 top();
                 soft(No{}, Yes{}, s - 1, s);
                 phase_barrier();
                 prod(Both{}, s);
+                prep(s + 1);
             }
             for (; s < steps; ++s) {
                 top();
                 soft(Yes{}, Yes{}, s - 1, s);
                 phase_barrier();
                 prod(Both{}, s);
+                prep(s + 1);
             }
             top();
             if (steps - 1 < sfull) soft(No{}, No{}, steps - 1, steps);

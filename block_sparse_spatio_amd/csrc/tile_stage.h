@@ -99,6 +99,20 @@ struct Stager {
         vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
 
+    // Chunk r of load() from source row srow (negative: read as zero), the
+    // row found by the caller.
+    __device__ __forceinline__ void load_chunk_at(int r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                                  int srow, int tid) {
+        const int u = tid + r * NT;
+        const int c = u % RV;
+        const int off = srow >= 0 ? srow * (D * 2) + c * 16 : 0x7ffffff0;
+        kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+
+    // Row of the sub-tile that chunk r of thread tid holds.
+    __device__ __forceinline__ static int chunk_row(int r, int tid) { return (tid + r * NT) / RV; }
+
     // Chunk r of store() alone (CH a multiple of NT).
     __device__ __forceinline__ void store_chunk(int r, char* stage, int tid) const {
         static_assert(CH % NT == 0, "every thread owns CU chunks");
