@@ -256,6 +256,38 @@ def test_split_tail(dev, wname, tiles, mode, gather):
             assert_close(bc[batch - 1, h].float().numpy(), ref, f"head {h}")
 
 
+def test_split_tail_workspace_reuse(dev):
+    """One split-tail workspace reused by a run of calls of different shapes, tile sizes and modes
+    (each leaves its pieces behind for the next): every call matches the unsplit launch, and a
+    repeated call reproduces its bits."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    qc, kc, vc = normal_qkv(2, w.heads, w.N, w.d, seed=8)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    flags = torch.tensor([list(w.kinds)] * 2, dtype=torch.uint8, device=dev)
+    ws = torch.full((B.svga_attn_split_workspace_bytes(w.d, 512),), 0x3C, dtype=torch.uint8, device=dev)
+    maps = {c: B.svga_build_tilemap(geom, mask, c[0], c[1], c[2], device=dev)
+            for c in ((256, 128, "exact"), (512, 128, "dense"), (256, 64, "rounded"))}
+    first = {}
+    for rnd in range(4):
+        for (bq, bkv, mode), tm in maps.items():
+            batch = 2 if (rnd + bq) % 2 == 0 else 1
+            args = (q[:batch], k[:batch], v[:batch], flags[:batch], tm, geom, mask, bq, bkv, mode)
+            a, la = B.svga_sparse_attn_fwd(*args, want_lse=True)
+            b, lb = B.svga_sparse_attn_fwd(*args, want_lse=True, workspace=ws)
+            torch.cuda.synchronize()
+            assert (a.float() - b.float()).abs().max().item() < 1e-2
+            fin = torch.isfinite(la)
+            assert torch.equal(fin, torch.isfinite(lb)) and (la[fin] - lb[fin]).abs().max().item() < 1e-4
+            key = (bq, bkv, mode, batch)
+            if key in first:
+                assert torch.equal(first[key].view(torch.int16), b.view(torch.int16))
+            else:
+                first[key] = b.clone()
+    say(f"split-tail workspace reuse: {len(first)} distinct calls, repeated calls bit-identical")
+
+
 def test_binding_rejects_bad_buffers(dev):
     """The binding refuses host tensors, short buffers and mismatched shapes before anything is
     launched (a host pointer or a short buffer handed to a kernel would be read out of bounds)."""
