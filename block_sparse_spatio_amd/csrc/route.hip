@@ -251,17 +251,28 @@ __global__ __launch_bounds__(D) void route_merge_kernel(RArgs a) {
     }
     if (t < 3) Lx[t] = red[t][0];
     __syncthreads();
+    // the three softmaxes' chunk loops fused, loads issued unconditionally and
+    // eight chunks ahead so that they overlap (each sum still runs in chunk
+    // order; a softmax whose max is -inf has no kept key and contributes 0)
+    float acc[3] = {0.f, 0.f, 0.f};
+    float mb[3];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) mb[x] = Mx[x] == -INFINITY ? 0.f : Mx[x];
+    constexpr size_t XS = (size_t)kMaxSamples * (D + 2);   // stride between the three softmaxes' partials
+    const float* w0 = a.ws + ws_index<D>(bh, 0, a.n_chunks, 0, n);
+    constexpr size_t CS = 3 * XS;                           // stride between chunks
+#pragma unroll 8
+    for (int c = 0; c < a.n_chunks; ++c) {
+        const float* w = w0 + (size_t)c * CS;
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const float e = w[x * XS + 2 + t] * __builtin_amdgcn_exp2f(w[x * XS] - mb[x]);
+            acc[x] += Mx[x] != -INFINITY ? e : 0.f;
+        }
+    }
     float o[3];
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
-        float acc = 0.f;
-        if (Mx[x] != -INFINITY)
-            for (int c = 0; c < a.n_chunks; ++c) {
-                const float* w = a.ws + ws_index<D>(bh, c, a.n_chunks, x, n);
-                acc += w[2 + t] * __builtin_amdgcn_exp2f(w[0] - Mx[x]);
-            }
-        o[x] = Lx[x] > 0.f ? acc / Lx[x] : 0.f;
-    }
+    for (int x = 0; x < 3; ++x) o[x] = Lx[x] > 0.f ? acc[x] / Lx[x] : 0.f;
     __syncthreads();
     red[0][t] = (o[1] - o[0]) * (o[1] - o[0]);
     red[1][t] = (o[2] - o[0]) * (o[2] - o[0]);
