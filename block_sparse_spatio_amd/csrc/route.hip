@@ -324,10 +324,12 @@ hipError_t launch_pair(const RArgs& r, int BH, hipStream_t stream) {
 void route_plan(int32_t BH, int32_t N, int32_t head_dim, int32_t n_samples, int32_t* chunk, int32_t* n_chunks,
                 size_t* ws_bytes) {
     (void)n_samples;
-    // About 512 workgroups in all (two per CU), chunks a multiple of 64 keys.
-    // Fewer, longer chunks keep the partials small (each chunk writes 3 x 64
-    // rows of D + 2 floats per head, which the merge reads back): measured
-    // fastest among 256 .. 2048 workgroups at 75,600 and 302,400 tokens.
+    // About 512 workgroups in all, chunks a multiple of 64 keys. Fewer, longer
+    // chunks keep the partials small (each chunk writes 3 x 64 rows of D + 2
+    // floats per head, which the merge reads back), more chunks spread the
+    // pass better: measured fastest among 256 .. 2048 workgroups at 75,600
+    // and 302,400 tokens (at 75,600: 256 -> 0.29 ms, 384 -> 0.22, 512 -> 0.19,
+    // 768 -> 0.20 for the partial pass).
     int64_t target = ((int64_t)N * BH + 511) / 512;
     int64_t c = (target + 63) / 64 * 64;
     if (c < 256) c = 256;
