@@ -157,6 +157,9 @@ static svga_status permute_common(const void* d_in, void* d_out, const uint8_t* 
     if (!d_in || !d_out || !d_flags) return fail(SVGA_EINVAL, "d_in, d_out and d_flags must be non-NULL");
     if (d_in == d_out) return fail(SVGA_EINVAL, "permutation is out of place: d_in == d_out");
     if (head_dim < 8 || head_dim > 512 || head_dim % 8) return fail(SVGA_EINVAL, "head_dim must be a multiple of 8 in [8, 512]");
+    const int64_t head_vecs = (int64_t)geom->F * geom->H * geom->W * (head_dim / 8);
+    if (head_vecs >= (int64_t(1) << 31))
+        return fail(SVGA_EINVAL, "N * head_dim / 8 = %lld must be below 2^31", (long long)head_vecs);
     Geo g = make_geo(*geom, *mask);
     (void)hipGetLastError();
     hipError_t e = launch_permute(d_in, d_out, d_flags, B * n_heads, g, head_dim, inverse, static_cast<hipStream_t>(stream));

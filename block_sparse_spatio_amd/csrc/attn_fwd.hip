@@ -56,6 +56,7 @@
 //   equal work. (Grouping consecutive query tiles on one XCD for L2 reuse
 //   measured slower: the XCDs' shares of work then differ and the last XCD
 //   sets the end, while K/V re-reads are cheap at this arithmetic intensity.)
+#include <atomic>
 #include <type_traits>
 
 #include "tile_stage.h"
@@ -730,6 +731,36 @@ __global__ __launch_bounds__(256) void merge_kernel(KArgs a, int rows) {
     if (a.lse && c == 0) a.lse[(size_t)bh * N + orow] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
+// Workgroups of one kernel instance that the current device holds at once
+// (CUs x occupancy), queried once per (instance, device) and cached: the
+// attribute and occupancy queries cost host time that every call would pay.
+constexpr int kMaxDevices = 64;
+template <int D, int QB, int WAVES, int KSUB, bool GATHER>
+hipError_t resident_workgroups(int* out) {
+    static std::atomic<int> cache[kMaxDevices];   // 0: not queried yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, GATHER>,
+                                                         WAVES * 64, 0);
+    if (e != hipSuccess) return e;
+    const int r = imax(cus, 1) * imax(per_cu, 1);
+    if (cached) cache[dev].store(r, std::memory_order_relaxed);
+    *out = r;
+    return hipSuccess;
+}
+
 template <int D, int QB, int WAVES, int KSUB>
 hipError_t launch_one(const KArgs& k0, bool gather, hipStream_t stream) {
     KArgs k = k0;
@@ -738,16 +769,10 @@ hipError_t launch_one(const KArgs& k0, bool gather, hipStream_t stream) {
     unsigned nwg = (unsigned)k.total;
     if (k.counter) {
         // as many workgroups as can be resident at once
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = gather ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                             &per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, true>, WAVES * 64, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                             &per_cu, attn_fwd_kernel<D, QB, WAVES, KSUB, false>, WAVES * 64, 0);
+        int resident = 0;
+        const hipError_t e = gather ? resident_workgroups<D, QB, WAVES, KSUB, true>(&resident)
+                                    : resident_workgroups<D, QB, WAVES, KSUB, false>(&resident);
         if (e != hipSuccess) return e;
-        const int resident = cus * imax(per_cu, 1);
         // split tail: the last min(resident, total) items (at most the
         // workspace's capacity) run in pieces
         const int nsplit = k.split && WAVES == kSplitWaves && QB == 1 ? imin(imin(resident, k.total), (int)kSplitItemsMax) : 0;

@@ -53,8 +53,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const uint4* __restri
 hipError_t launch_permute(const void* in, void* out, const uint8_t* flags, int32_t BH, const Geo& g, int32_t head_dim,
                           bool inverse, hipStream_t stream) {
     const int32_t row_vecs = head_dim / 8;
-    const int64_t head_vecs = (int64_t)g.N * row_vecs;
-    if (head_vecs >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    const int64_t head_vecs = (int64_t)g.N * row_vecs;   // below 2^31: checked by the caller
     FastDiv dv((uint32_t)row_vecs);
     dim3 grid((unsigned)((head_vecs + kThreads * kUnroll - 1) / (kThreads * kUnroll)), (unsigned)BH);
     hipLaunchKernelGGL(permute_kernel, grid, dim3(kThreads), 0, stream, static_cast<const uint4*>(in),

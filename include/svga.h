@@ -141,7 +141,8 @@ svga_status svga_build_tilemap_host(const svga_geom* geom, const svga_mask* mask
                                     void* h_map, size_t map_bytes);
 
 /* Same map, built by GPU kernels into DEVICE memory `d_map`, enqueued on `stream`.
- * Bit-identical to svga_build_tilemap_host. Needs tk <= 8192. */
+ * Bit-identical to svga_build_tilemap_host. Needs tk <= 8000 (the per-workgroup
+ * counters then fit 64 KB of LDS); SVGA_EUNSUPPORTED above that. */
 svga_status svga_build_tilemap(const svga_geom* geom, const svga_mask* mask,
                                int32_t bq, int32_t bkv, int32_t mode,
                                void* d_map, size_t map_bytes, void* stream);
@@ -153,7 +154,8 @@ svga_status svga_build_tilemap(const svga_geom* geom, const svga_mask* mask,
  * is nonzero, out[b,h,p(t),:] = in[b,h,t,:] with p the temporal order of
  * `mask->temporal_layout`; heads with flag 0 are copied unchanged. Out of
  * place: d_in and d_out are distinct device buffers of B*n_heads*N*head_dim
- * bf16. head_dim: a multiple of 8, at most 512. */
+ * bf16. head_dim: a multiple of 8, at most 512; N * head_dim / 8 (16-byte
+ * vectors per head) must stay below 2^31, else SVGA_EINVAL. */
 svga_status svga_permute(const void* d_in, void* d_out, const uint8_t* d_flags,
                          int32_t B, int32_t n_heads, const svga_geom* geom,
                          const svga_mask* mask, int32_t head_dim, void* stream);

@@ -47,13 +47,19 @@ def planted_qkv(batch, F, H, W, d, kinds, seed=0, strength=0.8, dtype=torch.bflo
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
-def census_qkv(batch, heads, N, d, dtype=torch.bfloat16):
-    """Q = 0 (uniform weights over each row's kept keys) and V[k, c] = 1 iff k mod d == c."""
+def census_qkv(batch, heads, N, d, key_class=None, dtype=torch.bfloat16):
+    """Q = K = 0 (uniform weights over each row's kept keys) and V[h, k, c] = 1 iff
+    key_class[h, k] mod d == c. ``key_class`` is an integer array [heads, N] chosen by the
+    caller (default: the key index k itself)."""
     q = torch.zeros(batch, heads, N, d, dtype=dtype)
     k = torch.zeros(batch, heads, N, d, dtype=dtype)
     v = torch.zeros(batch, heads, N, d, dtype=torch.float32)
     idx = torch.arange(N)
-    v[:, :, idx, idx % d] = 1.0
+    if key_class is None:
+        key_class = idx.expand(heads, N)
+    key_class = torch.as_tensor(key_class, dtype=torch.int64)
+    for h in range(heads):
+        v[:, h, idx, key_class[h] % d] = 1.0
     return q, k, v.to(dtype)
 
 

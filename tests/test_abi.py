@@ -79,6 +79,9 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.svga_permute(FAKE, FAKE, FAKE, 1, 2, g, m, 64, None) == -1
     assert L.svga_unpermute(FAKE, ctypes.c_void_p(0x2000), FAKE, 1, 2, g, m, 12, None) == -1
     assert L.svga_permute(FAKE, ctypes.c_void_p(0x2000), FAKE, 0, 2, g, m, 64, None) == -1
+    # 2^25 tokens x 512 dims: 2^31 16-byte vectors per head, past the kernel's 31-bit indexing
+    assert L.svga_permute(FAKE, ctypes.c_void_p(0x2000), FAKE, 1, 1, G(1 << 10, 1 << 10, 32), m, 512, None) == -1
+    assert b"2^31" in L.svga_last_error()
     # tile map on device: capacity, too many key tiles
     assert L.svga_build_tilemap(g, m, 32, 32, 2, FAKE, 100, None) == -3
     assert L.svga_build_tilemap(G(21, 90, 160), m, 32, 32, 2, FAKE, 1 << 40, None) == -2

@@ -27,14 +27,20 @@ def test_counter_records_match_the_committed_sources():
 
 
 def test_counter_records_go_stale_when_a_source_changes(tmp_path, monkeypatch):
+    """A record is reported while the listed sources hash to its digest, and not after an edit."""
+    import hashlib
     name = "attn_fwd_headline_exact_256x128_hbm_counters.md"
     text = open(os.path.join(ROOT, "profiles", name)).read()
     rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
     os.makedirs(tmp_path / "profiles")
-    shutil.copy(os.path.join(ROOT, "profiles", name), tmp_path / "profiles" / name)
+    h = hashlib.sha256()
     for f in rec["sources"]:
         os.makedirs(tmp_path / os.path.dirname(f), exist_ok=True)
         shutil.copy(os.path.join(ROOT, f), tmp_path / f)
+        h.update(open(tmp_path / f, "rb").read())
+    rec["sources_sha256"] = h.hexdigest()   # a record taken from exactly these sources
+    with open(tmp_path / "profiles" / name, "w") as fh:
+        fh.write("```json\n" + json.dumps(rec) + "\n```\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.counted_traffic("exact", 256, 128) == rec["traffic_bytes"]
     with open(tmp_path / rec["sources"][0], "a") as fh:

@@ -35,18 +35,20 @@ def i16(t):
     return t.contiguous().view(torch.int16).cpu().numpy()
 
 
-def run_attention(dev, geom, mask, q, k, v, kinds, bq, bkv, mode, gather=False, want_lse=False):
-    """Frame-major in, frame-major out: permute -> attention -> unpermute (or the in-kernel gather)."""
+def run_attention(dev, geom, mask, q, k, v, kinds, bq, bkv, mode, gather=False, want_lse=False, workspace=None):
+    """Frame-major in, frame-major out: permute -> attention -> unpermute (or the in-kernel gather).
+    LSE rows come back in frame-major order too."""
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     Bn = q.shape[0]
     flags = torch.tensor([list(kinds)] * Bn, dtype=torch.uint8, device=dev)
     tm = B.svga_build_tilemap(geom, mask, bq, bkv, mode, device=dev)
     if gather:
         o, lse = B.svga_sparse_attn_fwd(qd, kd, vd, flags, tm, geom, mask, bq, bkv, mode, gather_temporal=True,
-                                        want_lse=want_lse)
+                                        want_lse=want_lse, workspace=workspace)
     else:
         qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (qd, kd, vd))
-        op, lsep = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode, want_lse=want_lse)
+        op, lsep = B.svga_sparse_attn_fwd(qp, kp, vp, flags, tm, geom, mask, bq, bkv, mode, want_lse=want_lse,
+                                          workspace=workspace)
         o = B.svga_unpermute(op, flags, geom, mask)
         lse = None
         if want_lse:
@@ -352,25 +354,45 @@ def test_naive_and_exact_agree(dev):
                 assert np.array_equal(i16(a[0, h]), i16(b[0, h]))
 
 
+def key_tile_classes(w, mask, kinds, bkv):
+    """[heads, N]: the key tile of each frame-major key in its head's executed order."""
+    out = np.empty((len(kinds), w.N), dtype=np.int64)
+    for h, kind in enumerate(kinds):
+        out[h] = O.positions(O.executed_order(w.F, w.H, w.W, kind, mask[0], mask[3])) // bkv
+    return out
+
+
+@pytest.mark.parametrize("tiles,split", [((128, 128), False), ((256, 128), True), ((512, 64), True)])
+@pytest.mark.parametrize("form", ["tile", "residue"])
 @pytest.mark.parametrize("mode", [1, 2, 3])
-def test_census_counts_every_kept_key(dev, mode):
-    """Q = 0: uniform weights over each row's kept keys; V[k, c] = [k mod d == c]; the output is the
-    exact share of kept keys per residue class. A missing or extra tile moves a column by far more
-    than bf16 rounding."""
+def test_census_counts_every_kept_key(dev, mode, form, tiles, split):
+    """Q = K = 0: uniform weights over each row's kept keys, so the output is an exact rational.
+    form "tile": V[k, c] = [kv_tile(k) mod d == c] with kv_tile the key's tile in the executed
+    order; here every one of the 27 (or 54) key tiles has a column of its own (d = 128), so a
+    dropped or doubled key tile moves its column from its share to 0 or to twice its share.
+    form "residue": V[k, c] = [k mod d == c] (catches single keys misplaced inside a tile on
+    temporal heads). LSE must equal ln(kept keys): one 64-key tile more or less moves it by at
+    least 64/3456, against a bar of 1e-4. Every row of all four heads, in the plain launch and in
+    the persistent launch with the split tail (every work item split at 3,456 tokens)."""
     w = SMALL
+    bq, bkv = tiles
     geom = (w.F, w.H, w.W)
     mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
-    say(f"census small mode={mode}")
-    q, k, v = census_qkv(1, w.heads, w.N, w.d)
-    o, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, w.bq, w.bkv, mode)
+    say(f"census small mode={mode} form={form} tiles={tiles} split={split}")
+    cls = key_tile_classes(w, mask, w.kinds, bkv) if form == "tile" else None
+    q, k, v = census_qkv(1, w.heads, w.N, w.d, key_class=cls)
+    ws = torch.zeros(B.svga_attn_split_workspace_bytes(w.d, bq), dtype=torch.uint8, device=dev) if split else None
+    o, lse = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, want_lse=True, workspace=ws)
     rows = np.arange(w.N)
     for h, kind in enumerate(w.kinds):
-        ref, _ = oracle_head(geom, mask, q[0, h], k[0, h], v[0, h], kind, mode, w.bq, w.bkv, 0.1, rows=rows)
+        ref, ref_lse = oracle_head(geom, mask, q[0, h], k[0, h], v[0, h], kind, mode, bq, bkv, 0.1, rows=rows)
         got = o[0, h].float().numpy()
         rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)
-        say(f"  head {h}: max rel {rel[ref > 0].max():.3e}")
+        lerr = np.abs(lse[0, h].numpy() - ref_lse)
+        say(f"  head {h}: max rel {rel[ref > 0].max():.3e}, LSE max err {lerr.max():.3e}")
         assert (got[ref == 0] == 0).all()
         assert rel[ref > 0].max() < 2 ** -7
+        assert lerr.max() < 1e-4
 
 
 @pytest.mark.parametrize("geom,mask,tiles,kinds", [

@@ -5,6 +5,7 @@ closed form derived from the mask definitions, an independent interval count,
 a library routine (torch scaled_dot_product_attention, scipy logsumexp), or a
 brute-force loop on a tiny case.
 """
+import json
 import math
 import os
 
@@ -406,3 +407,105 @@ def test_routing_finds_planted_head_kinds():
     flags, err = O.route_heads(q.float().numpy(), k.float().numpy(), v.float().numpy(),
                                F, H, W, 1, 1, 24, idx, 1 / math.sqrt(d))
     assert tuple(flags[0]) == kinds
+
+
+# ---------------------------------------------------------------- balanced rounding (B3)
+
+# Tile statistics from an independent per-row interval calculation made before
+# any of this code (not from the pages, whose band widths are lost): the class
+# totals of the exact classification (FULL, BOUNDARY, SKIP, kept pairs) and of
+# the balanced rounding (FULL, BOUNDARY, kept pairs). Keyed by
+# (workload, kind, bq, bkv); geometry and masks as in synth.workloads.
+INDEPENDENT_COUNTS = {
+    ("tiny", 0, 32, 32): ((12, 0, 4, 12_288), (12, 0, 12_288)),
+    ("tiny", 1, 32, 32): ((4, 10, 2, 5_944), (4, 0, 4_096)),
+    ("small", 0, 128, 128): ((288, 0, 441, 4_718_592), (288, 0, 4_718_592)),
+    ("small", 1, 128, 128): ((105, 122, 502, 2_638_656), (151, 0, 2_473_984)),
+    ("headline", 0, 128, 128): ((145_514, 2_083, 201_684, 2_397_600_000), (146_358, 141, 2_398_337_280)),
+    ("headline", 1, 128, 128): ((123_134, 3_608, 222_539, 2_046_668_400), (124_666, 106, 2_042_822_912)),
+    ("headline", 0, 256, 128): ((72_616, 1_478, 100_842, 2_397_600_000), (73_274, 71, 2_398_697_728)),
+    ("headline", 1, 256, 128): ((61_110, 2_830, 110_996, 2_046_668_400), (62_637, 53, 2_050_676_992)),
+    ("headline", 0, 512, 128): ((36_013, 1_202, 50_253, 2_397_600_000), (36_705, 36, 2_403_174_656)),
+    ("headline", 1, 512, 128): ((30_034, 2_438, 54_996, 2_046_668_400), (31_319, 27, 2_050_707_712)),
+}
+WORKLOAD_ARGS = {   # F, H, W, sink, spatial band, temporal band, layout
+    "tiny": (4, 4, 8, 1, 1, 2, 0),
+    "small": (9, 16, 24, 1, 1, 24, 0),
+    "headline": (21, 45, 80, 1, 4, 644, 0),
+}
+
+
+def _b3_totals(r):
+    kept = r["cls"] != O.SKIP
+    return (int((r["cls"] == O.FULL).sum()), int((r["cls"] == O.BOUNDARY).sum()), int((r["area"] * kept).sum()))
+
+
+@pytest.mark.parametrize("key", [k for k in INDEPENDENT_COUNTS if k[0] != "headline"],
+                         ids=lambda k: f"{k[0]}-{'spatial' if k[1] == 0 else 'temporal'}-{k[2]}x{k[3]}")
+def test_rounding_matches_independent_counts(key):
+    """Pin: the oracle's exact and balanced-rounding (B3) classifications, run here by element scan,
+    reproduce the independent interval counts above: FULL / BOUNDARY / SKIP totals and kept pairs.
+    The rounding rule (keep a tile iff it holds a kept pair and kept pairs fill at least half its
+    valid area) is fixed by these numbers: rounding every boundary tile outward keeps 227 tiles and
+    3,719,168 pairs at the small temporal size, inward 105 tiles, against 151 and 2,473,984."""
+    name, kind, bq, bkv = key
+    F, H, W, sink, bs, bt, lay = WORKLOAD_ARGS[name]
+    counts = O.tile_counts(F, H, W, kind, sink, bs, bt, lay, bq, bkv)
+    ex = O.classify(F, H, W, kind, sink, bs, bt, lay, bq, bkv, O.MODE_EXACT, counts=counts)
+    rd = O.classify(F, H, W, kind, sink, bs, bt, lay, bq, bkv, O.MODE_ROUNDED, counts=counts)
+    want_ex, want_rd = INDEPENDENT_COUNTS[key]
+    got_ex = (int((ex["cls"] == O.FULL).sum()), int((ex["cls"] == O.BOUNDARY).sum()),
+              int((ex["cls"] == O.SKIP).sum()), int(counts.sum()))
+    assert got_ex == want_ex
+    assert _b3_totals(rd) == want_rd
+
+
+@pytest.mark.parametrize("bq", [128, 256, 512])
+def test_headline_rounding_goldens_match_independent_counts(bq):
+    """Pin: the 75,600-token tile totals that tests/golden/make_tilemap_golden.py wrote with the
+    oracle's element scan (about 40 s per head kind, so stored rather than rerun here) equal the
+    independent interval counts, for the exact and the balanced-rounding classification."""
+    g = json.load(open(os.path.join(GOLDEN, f"tilemap_headline_{bq}x128.json")))
+    assert (g["F"], g["H"], g["W"], g["sink_frames"], g["spatial_band"], g["temporal_band"],
+            g["temporal_layout"]) == WORKLOAD_ARGS["headline"]
+    for kind, kname in ((0, "spatial"), (1, "temporal")):
+        want_ex, want_rd = INDEPENDENT_COUNTS[("headline", kind, bq, 128)]
+        ex, rd = g["kinds"][kname]["exact"], g["kinds"][kname]["rounded"]
+        assert (ex["full"], ex["boundary"], ex["skip"], ex["retained_pairs"]) == want_ex
+        assert (rd["full"], rd["boundary"], rd["retained_pairs"]) == want_rd
+
+
+@pytest.mark.parametrize("tiles", [(128, 128), (64, 64), (256, 128), (96, 64)])
+@pytest.mark.parametrize("kind", [0, 1])
+def test_rounding_keeps_the_pair_budget(kind, tiles):
+    """Pin: the page asks balanced rounding to keep the kept-pair budget approximately. At the small
+    workload (3,456 tokens) the rounded mask keeps within 10% of the exact mask's pairs, and at the
+    75,600-token workload (stored totals) within 1%; outward-only rounding keeps 41% more at the
+    small temporal size. Every all-kept tile stays and no all-excluded tile is added."""
+    F, H, W, sink, bs, bt, lay = WORKLOAD_ARGS["small"]
+    bq, bkv = tiles
+    args = (F, H, W, kind, sink, bs, bt, lay, bq, bkv)
+    counts = O.tile_counts(*args)
+    ex = O.classify(*args, O.MODE_EXACT, counts=counts)
+    rd = O.classify(*args, O.MODE_ROUNDED, counts=counts)
+    exact_pairs = int(counts.sum())
+    rounded_pairs = _b3_totals(rd)[2]
+    assert abs(rounded_pairs - exact_pairs) <= 0.10 * exact_pairs, (rounded_pairs, exact_pairs)
+    assert (rd["cls"][ex["cls"] == O.FULL] == O.FULL).all()
+    assert (rd["cls"][ex["cls"] == O.SKIP] == O.SKIP).all()
+    for (name, k, _, _), (want_ex, want_rd) in INDEPENDENT_COUNTS.items():
+        if name == "headline":
+            assert abs(want_rd[2] - want_ex[3]) <= 0.01 * want_ex[3]
+
+
+def test_rounding_tie_by_hand():
+    """Pin: a hand-counted tie. Two frames of 4 tokens, spatial band 0, no sink, one 8 x 8 tile:
+    each query keeps the 4 keys of its own frame, so 32 of the 64 pairs are kept, exactly half.
+    The adopted reading keeps ties (rounds them outward), so the whole tile is kept, FULL."""
+    c = O.tile_counts(2, 1, 4, O.KIND_SPATIAL, 0, 0, 0, 0, 8, 8)
+    assert c.tolist() == [[32]]
+    rd = O.classify(2, 1, 4, O.KIND_SPATIAL, 0, 0, 0, 0, 8, 8, O.MODE_ROUNDED)
+    assert rd["cls"].tolist() == [[O.FULL]]
+    # one key fewer per row (3 x 4 tokens, band 0: 3 x 16 = 48 of 144 pairs) rounds inward
+    rd = O.classify(3, 1, 4, O.KIND_SPATIAL, 0, 0, 0, 0, 12, 12, O.MODE_ROUNDED)
+    assert rd["cls"].tolist() == [[O.SKIP]]
