@@ -47,6 +47,8 @@ SIGNATURES = {
     "svga_attn_split_workspace_bytes": (c_i32, [c_i32, c_i32, ctypes.POINTER(c_size)]),
     "svga_sparse_attn_fwd_ws": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, G, M, c_i32, c_f32, c_vp, c_vp,
                                         c_size, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "svga_sparse_attn_fwd_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, G, M, c_i32, c_f32, c_vp,
+                                             c_vp, c_size, c_i32, c_i32, c_i32, c_i32, c_vp]),
 }
 
 _lib = None

@@ -95,7 +95,7 @@ const char* svga_status_string(svga_status s) {
 
 const char* svga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t svga_version(void) { return 102; }
+int32_t svga_version(void) { return 103; }
 
 svga_status svga_tilemap_layout(const svga_geom* geom, int32_t bq, int32_t bkv, svga_tilemap_offsets* out) {
     TRY(check_geom(geom));
@@ -224,7 +224,7 @@ static svga_status attn_common(const char* who, const void* d_q, const void* d_k
                                float* d_lse, int32_t B, int32_t n_heads, const svga_geom* geom, const svga_mask* mask,
                                int32_t head_dim, float softmax_scale, const uint8_t* d_flags, const void* d_map,
                                size_t map_bytes, int32_t bq, int32_t bkv, int32_t mode, int32_t gather_temporal,
-                               int32_t* d_counter, int32_t split, void* stream) {
+                               int32_t* d_counter, int32_t split, void* stream, bool check_only = false) {
     TRY(check_geom(geom));
     TRY(check_mask(mask, geom));
     TRY(check_heads(B, n_heads));
@@ -246,6 +246,7 @@ static svga_status attn_common(const char* who, const void* d_q, const void* d_k
     Geo g = make_geo(*geom, *mask);
     MapLayout L = map_layout(g.N, bq, bkv);
     if (map_bytes < L.total) return fail(SVGA_ECAPACITY, "map_bytes %zu < required %zu", map_bytes, L.total);
+    if (check_only) return SVGA_OK;
     AttnLaunch a{};
     a.q = d_q;
     a.k = d_k;
@@ -315,4 +316,31 @@ svga_status svga_sparse_attn_fwd_ws(const void* d_q, const void* d_k, const void
                        static_cast<int32_t*>(d_workspace), split, stream);
 }
 
+svga_status svga_sparse_attn_fwd_noalloc(const void* d_q, const void* d_k, const void* d_v, void* d_o, float* d_lse,
+                                         int32_t B, int32_t n_heads, const svga_geom* geom, const svga_mask* mask,
+                                         int32_t head_dim, float softmax_scale, const uint8_t* d_flags,
+                                         const void* d_map, size_t map_bytes, int32_t bq, int32_t bkv, int32_t mode,
+                                         int32_t gather_temporal, void* stream) {
+    // the scratch needs of a call depend on head_dim and bq only; every supported pair fits
+    if (attn_supported(head_dim, bq, bkv) && attn_split_workspace_bytes(head_dim, bq) > kNoAllocScratchBytes)
+        return fail(SVGA_ECAPACITY, "head_dim=%d bq=%d needs %zu scratch bytes, more than the %zu this entry point holds",
+                    head_dim, bq, attn_split_workspace_bytes(head_dim, bq), kNoAllocScratchBytes);
+    // argument checks first, so that an invalid call touches no device state
+    {
+        svga_status st = attn_common("svga_sparse_attn_fwd_noalloc", d_q, d_k, d_v, d_o, d_lse, B, n_heads, geom,
+                                     mask, head_dim, softmax_scale, d_flags, d_map, map_bytes, bq, bkv, mode,
+                                     gather_temporal, nullptr, 0, nullptr, /*check_only=*/true);
+        if (st != SVGA_OK) return st;
+    }
+    void* scratch = nullptr;
+    (void)hipGetLastError();
+    hipError_t e = noalloc_scratch(&scratch);
+    if (e != hipSuccess) return fail(SVGA_EHIP, "svga_sparse_attn_fwd_noalloc: scratch lookup: %s", hipGetErrorString(e));
+    const int32_t split = attn_supported(head_dim, bq, bkv) && bq >= 32 * kSplitWaves ? 1 : 0;
+    return attn_common("svga_sparse_attn_fwd_noalloc", d_q, d_k, d_v, d_o, d_lse, B, n_heads, geom, mask, head_dim,
+                       softmax_scale, d_flags, d_map, map_bytes, bq, bkv, mode, gather_temporal,
+                       static_cast<int32_t*>(scratch), split, stream, false);
+}
+
 }  // extern "C"
+

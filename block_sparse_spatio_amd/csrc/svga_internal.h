@@ -258,6 +258,12 @@ inline size_t attn_split_workspace_bytes(int32_t head_dim, int32_t bq) {
     return kSplitLseOffset + split_lse_bytes(bq) + kSplitItemsMax * kSplitParts * split_rows(bq) * head_dim * 2;
 }
 bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv);
+// Scratch of svga_sparse_attn_fwd_noalloc: the split-tail workspace of the
+// largest supported case (head_dim 128, 256-row workgroups), 68,157,696 bytes.
+constexpr size_t kNoAllocScratchBytes =
+    kSplitLseOffset + kSplitItemsMax * kSplitParts * 256 * 4 + kSplitItemsMax * kSplitParts * 256 * 128 * 2;
+// Device address of this device's scratch array (looked up on first use per device).
+hipError_t noalloc_scratch(void** out);
 
 hipError_t launch_permute(const void* in, void* out, const uint8_t* flags, int32_t BH, const Geo& g,
                           int32_t head_dim, bool inverse, hipStream_t stream);

@@ -213,12 +213,16 @@ def svga_attn_split_workspace_bytes(head_dim, bq):
 
 
 def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, softmax_scale=None,
-                         gather_temporal=False, out=None, lse=None, want_lse=False, workspace=None, stream=None):
+                         gather_temporal=False, out=None, lse=None, want_lse=False, workspace=None, stream=None,
+                         noalloc=False):
     """Block-sparse attention forward. Returns (out, lse); lse is None unless requested.
     With `workspace` (a 16-byte aligned device tensor of at least svga_attn_workspace_bytes() bytes)
     the call runs persistent workgroups (svga_sparse_attn_fwd_ws): the same bits as without it, unless
     the workspace holds svga_attn_split_workspace_bytes(d, bq) bytes, in which case the last query
-    tiles run in pieces merged through their softmax statistics (equal up to rounding)."""
+    tiles run in pieces merged through their softmax statistics (equal up to rounding).
+    With `noalloc=True` (and no workspace) the call is svga_sparse_attn_fwd_noalloc: the launch of the
+    split-tail workspace, on the library's own per-GPU scratch array (the library allocates nothing;
+    calls on one GPU must not overlap). `out` and `lse`, when given, are then the only buffers used."""
     _qkv_check(q, k, v)
     B, H, N, d = q.shape
     out = torch.empty_like(q) if out is None else out
@@ -233,7 +237,11 @@ def svga_sparse_attn_fwd(q, k, v, flags, tilemap, geom, mask, bq, bkv, mode, sof
     args = (_vp(q), _vp(k), _vp(v), _vp(out), _vp(lse), B, H, ctypes.byref(_geom(geom)), ctypes.byref(_mask(mask)), d,
             float(scale), _vp(flags), _vp(tilemap), tilemap.numel() * tilemap.element_size(), int(bq), int(bkv),
             _mode(mode), 1 if gather_temporal else 0)
-    if workspace is None:
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc=True takes no workspace")
+        _check(lib().svga_sparse_attn_fwd_noalloc(*args, _stream(stream)))
+    elif workspace is None:
         _check(lib().svga_sparse_attn_fwd(*args, _stream(stream)))
     else:
         _check(lib().svga_sparse_attn_fwd_ws(*args, _vp(workspace), workspace.numel() * workspace.element_size(),

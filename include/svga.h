@@ -271,6 +271,30 @@ svga_status svga_sparse_attn_fwd_ws(const void* d_q, const void* d_k, const void
                                     int32_t gather_temporal, void* d_workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The operation
+ * and launch of svga_sparse_attn_fwd_ws with a split-tail workspace (same
+ * kernels, same bits), with the library's own scratch memory in place of the
+ * workspace: one file-scope device array of 68,157,696 bytes per GPU (the
+ * work counter plus the split tail of the largest supported case, head_dim
+ * 128 and 256-row workgroups), which that GPU holds from the first call on it
+ * until the process ends. The call allocates and frees nothing; the scratch
+ * address is looked up once per device, on the first call with that device
+ * current. Every call on one GPU uses the same scratch, and the call clears
+ * what must start at zero (the work counter) on `stream` itself: calls on one
+ * GPU that may overlap (different streams without ordering, several host
+ * threads) race on it and must be serialised by the caller. Arguments and
+ * errors as svga_sparse_attn_fwd; SVGA_ECAPACITY if a configuration would
+ * need more scratch than the array holds (none of the supported head_dim and
+ * bq values does); SVGA_EHIP if the scratch address cannot be found. */
+svga_status svga_sparse_attn_fwd_noalloc(const void* d_q, const void* d_k, const void* d_v,
+                                         void* d_o, float* d_lse,
+                                         int32_t B, int32_t n_heads, const svga_geom* geom,
+                                         const svga_mask* mask, int32_t head_dim, float softmax_scale,
+                                         const uint8_t* d_flags, const void* d_map, size_t map_bytes,
+                                         int32_t bq, int32_t bkv, int32_t mode,
+                                         int32_t gather_temporal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

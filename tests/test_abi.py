@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == len(_lib.SIGNATURES) == 14
+    assert len(names) == len(_lib.SIGNATURES) == 15
     assert set(names) == set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(L, n), n
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.svga_version() == 102
+    assert L.svga_version() == 103
     assert L.svga_status_string(0) == b"ok"
     assert L.svga_status_string(-3) == b"buffer too small"
 
@@ -124,6 +124,12 @@ def test_device_entry_points_reject_bad_arguments_before_launch():
     assert L.svga_attn_split_workspace_bytes(128, 256, None) == -1
     bad = (*a, o, None, 1, 2, g, m, 96, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, 32, 32, 2, 0)
     assert L.svga_sparse_attn_fwd_ws(*bad, FAKE, n.value, None) == -2
+    # no-alloc variant: the same host checks, before any device state is touched
+    assert L.svga_sparse_attn_fwd_noalloc(*bad, None) == -2
+    assert L.svga_sparse_attn_fwd_noalloc(*a, FAKE, None, 1, 2, g, m, 64, ctypes.c_float(0.1), FAKE, FAKE, 1 << 20,
+                                          32, 32, 2, 0, None) == -1
+    assert L.svga_sparse_attn_fwd_noalloc(*a, o, None, 1, 2, g, m, 64, ctypes.c_float(0.1), FAKE, FAKE, 100,
+                                          32, 32, 2, 0, None) == -3
 
 
 def test_python_binding_raises_with_message():
