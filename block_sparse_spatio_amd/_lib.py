@@ -33,6 +33,8 @@ SIGNATURES = {
     "svga_status_string": (ctypes.c_char_p, [c_i32]),
     "svga_last_error": (ctypes.c_char_p, []),
     "svga_version": (c_i32, []),
+    "svga_mask_for_kept_fraction": (c_i32, [G, c_i32, c_i32, ctypes.c_double, ctypes.c_double, M,
+                                            ctypes.POINTER(ctypes.c_int64)]),
     "svga_tilemap_layout": (c_i32, [G, c_i32, c_i32, ctypes.POINTER(SvgaTilemapOffsets)]),
     "svga_build_tilemap_host": (c_i32, [G, M, c_i32, c_i32, c_i32, c_vp, c_size]),
     "svga_build_tilemap": (c_i32, [G, M, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsvga.so")
-SOURCES = ["api.cpp", "tilemap_host.cpp", "tilemap.hip", "permute.hip", "attn_fwd.hip", "route.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "tilemap_host.cpp", "plan_host.cpp", "tilemap.hip", "permute.hip", "attn_fwd.hip", "route.hip", "noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

@@ -95,7 +95,7 @@ const char* svga_status_string(svga_status s) {
 
 const char* svga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t svga_version(void) { return 103; }
+int32_t svga_version(void) { return 104; }
 
 svga_status svga_tilemap_layout(const svga_geom* geom, int32_t bq, int32_t bkv, svga_tilemap_offsets* out) {
     TRY(check_geom(geom));
@@ -109,6 +109,26 @@ svga_status svga_tilemap_layout(const svga_geom* geom, int32_t bq, int32_t bkv, 
     out->total = L.total;
     out->tq = L.tq;
     out->tk = L.tk;
+    return ok();
+}
+
+svga_status svga_mask_for_kept_fraction(const svga_geom* geom, int32_t sink_frames, int32_t temporal_layout,
+                                        double spatial_target, double temporal_target, svga_mask* out,
+                                        int64_t* kept_pairs) {
+    TRY(check_geom(geom));
+    if (!out) return fail(SVGA_EINVAL, "out is NULL");
+    if (!(spatial_target >= 0.0 && spatial_target <= 1.0) || !(temporal_target >= 0.0 && temporal_target <= 1.0))
+        return fail(SVGA_EINVAL, "targets must be in [0, 1] (got %g, %g)", spatial_target, temporal_target);
+    svga_mask m{sink_frames, 0, 0, temporal_layout};
+    TRY(check_mask(&m, geom));
+    const int64_t S = (int64_t)geom->H * geom->W;
+    m.spatial_band = band_for_kept_fraction(SVGA_KIND_SPATIAL, geom->F, S, sink_frames, spatial_target);
+    m.temporal_band = band_for_kept_fraction(SVGA_KIND_TEMPORAL, geom->F, S, sink_frames, temporal_target);
+    *out = m;
+    if (kept_pairs) {
+        kept_pairs[0] = kept_pairs_spatial(geom->F, S, sink_frames, m.spatial_band);
+        kept_pairs[1] = kept_pairs_temporal(geom->F, S, sink_frames, m.temporal_band);
+    }
     return ok();
 }
 

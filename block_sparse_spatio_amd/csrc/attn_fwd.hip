@@ -837,12 +837,6 @@ hipError_t dispatch(const KArgs& k, int bq, int ksub, bool gather, hipStream_t s
 
 }  // namespace
 
-bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv) {
-    if (head_dim != 64 && head_dim != 128) return false;
-    if (!(bq == 32 || bq == 64 || bq == 128 || bq == 256 || bq == 512)) return false;
-    return bkv >= 32 && bkv <= 512 && bkv % 32 == 0;
-}
-
 hipError_t launch_attn_fwd(const AttnLaunch& a, hipStream_t stream, bool* supported) {
     *supported = attn_supported(a.head_dim, a.bq, a.bkv);
     if (!*supported) return hipSuccess;

@@ -7,31 +7,45 @@
 // tensor shapes": the result is a Boolean flag per head that stays on the
 // device.
 //
-// Pass 1 (route_partial_kernel): one workgroup per (batch*head, key chunk).
-// Each wave holds 32 sampled queries as MFMA B operands and runs one of the
-// three softmaxes (dense, spatial mask, temporal mask) with its own running
-// max, sum and output; every K/V sub-tile of the chunk is staged through LDS
-// once and serves all waves. The softmax kind is wave-uniform, so each wave
-// runs a loop specialised to it; its mask is a 64-bit keep mask over the
-// step's keys (built from at most two key ranges, or from the frames the step
-// touches) and costs a bit test per score. P is split into a bf16 high part
-// and a bf16 remainder, both fed to the MFMA, so the weighted sums keep about
-// 16 mantissa bits. The partial (max, sum, output) of every softmax is
-// written to the workspace.
+// Pass 1 (route_partial_kernel): one workgroup per (batch*head, key chunk),
+// about one per CU in all. The chunk is split in two halves, each walked by
+// its own waves over its own double-buffered LDS stage; each wave holds 32
+// sampled queries as MFMA B operands. Per step of KSUB keys a wave computes
+// the scores S^T = K Q^T once and feeds all three softmaxes (dense, spatial
+// mask, temporal mask) from them: the three share one running exponent base
+// (the dense running maximum, rescaled lazily), so each score costs one
+// exponential, and the masked probabilities are the dense ones with excluded
+// keys set to zero. P is split into a bf16 high part and a bf16 remainder,
+// both fed to the MFMA, so the weighted sums keep about 16 mantissa bits:
+// 7 products of 2*d FLOP per (sample, key) (one for the scores, two for each
+// softmax's output). Masks are 64-bit keep masks over the step's keys (from
+// at most two key ranges, or from the frames the step touches), a bit test
+// per score. At the end the two halves merge in LDS and the workgroup writes
+// one partial (exponent base, three sums, three unnormalised outputs) per
+// sample.
 // Pass 2 (route_merge_kernel): one workgroup per (sample, batch*head) merges
 // the chunk partials and forms that sample's ||o_x - o_dense||^2.
 // Pass 3 (route_flag_kernel): err_x = sum over samples, in sample order; the
 // flag is 1 (temporal) iff err_temporal < err_spatial.
 // Memory traffic: K and V read once; roofline is HBM bandwidth.
+//
+// The shared base is the dense maximum, which is at least each masked
+// maximum, so masked probabilities are exact fractions of it; a sample whose
+// kept scores all lie more than 126 (in log2 units of the scaled scores)
+// below its dense maximum would underflow to an empty masked softmax.
 #include <type_traits>
 
 #include "tile_stage.h"
 
 namespace svga {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 namespace {
 
-constexpr int kMaxSamples = 64;
+constexpr int kMaxSamples = kRouteMaxSamples;
+constexpr int kRouteParts = 2;   // key halves per workgroup
+constexpr int kRouteBlocks = 4;  // blocks of 16 sampled queries (kMaxSamples = 64)
 
 struct RArgs {
     const uint16_t* q;
@@ -52,160 +66,324 @@ __device__ __forceinline__ size_t ws_index(int bh, int chunk, int n_chunks, int 
     return ((((size_t)bh * n_chunks + chunk) * 3 + x) * kMaxSamples + n) * (D + 2);
 }
 
-// QBLK blocks of 32 samples; wave w serves sample block w / 3 under softmax
-// kind w % 3 (0 dense, 1 spatial mask, 2 temporal mask).
-template <int D, int QBLK, int KSUB>
-__global__ __launch_bounds__(QBLK * 3 * 64) void route_partial_kernel(RArgs a) {
-    constexpr int NT = QBLK * 3 * 64;
-    constexpr int KBLK = KSUB / 32;
-    constexpr int DB = D / 32;
-    constexpr int DC = D / 16;
-    using St = Stager<D, KSUB, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * St::STAGE];
+// Bits [a - base, b - base) of a 32-bit mask over keys base .. base+31 (clamped).
+__device__ __forceinline__ uint32_t window_bits32(int a, int b, int base) {
+    const int lo = imin(imax(a - base, 0), 32), hi = imin(imax(b - base, 0), 32);
+    const uint32_t below_hi = hi >= 32 ? ~0u : (1u << hi) - 1u;
+    const uint32_t below_lo = lo >= 32 ? ~0u : (1u << lo) - 1u;
+    return below_hi & ~below_lo;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The other values of x among the four lanes l % 16 + 16 j (lane-row swaps
+// of v_permlane16_swap and v_permlane32_swap: each returns the partner row's
+// value in one of its two results, whichever lane calls it).
+__device__ __forceinline__ float swap16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0] == u ? (uint32_t)r[1] : (uint32_t)r[0]);
+}
+__device__ __forceinline__ float swap32(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0] == u ? (uint32_t)r[1] : (uint32_t)r[0]);
+}
+__device__ __forceinline__ float group_max(float x) {
+    x = fmaxf(x, swap16(x));
+    return fmaxf(x, swap32(x));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    x += swap16(x);
+    return x + swap32(x);
+}
+
+// Two bf16 (round to nearest even) packed in one word, x in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+    const bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 0xffff in each half of pair j whose bit (2j, 2j+1) of bits is set.
+__device__ __forceinline__ uint32_t pair_mask(uint32_t bits, int j) {
+    return ((bits >> (2 * j)) & 1u ? 0x0000ffffu : 0u) | ((bits >> (2 * j + 1)) & 1u ? 0xffff0000u : 0u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
+    return __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
+}
+
+constexpr float kRouteRescaleLog2 = 8.0f;   // new base when the running max grows by more than 2^8
+
+// Waves: kRouteBlocks blocks of 16 samples x kRouteParts key halves; wave
+// w serves sample block w % kRouteBlocks over key half w / kRouteBlocks.
+// Products are v_mfma_f32_16x16x32_bf16 (lane l holds row / column l % 16
+// and the 8 consecutive reduction elements 8 (l / 16) .. +7 of its A / B
+// operand, and rows 4 (l / 16) .. +3 of column l % 16 of the result):
+// * S^T = K Q^T in two chains of 16 keys (keys 16 j .. 16 j + 15), so lane
+//   group g = l / 16 ends up with the scores of keys 4 g .. 4 g + 3 and
+//   16 + 4 g .. + 3 of its sample: the B operand of
+// * O^T = V^T P^T per block of 16 dimensions, whose reduction runs over the
+//   step's keys in that same order: V^T comes from two transposing LDS reads
+//   (keys 4 g .. 4 g + 3 and 16 + 4 g .. + 3).
+// Each lane then owns 8 (sample, key) scores per 32-key step and 3 * D / 16
+// accumulator registers, so two waves share each SIMD.
+template <int D>
+__global__ __launch_bounds__(kRouteBlocks * kRouteParts * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void route_partial_kernel(RArgs a) {
+    constexpr int KSUB = 32;
+    constexpr int PT = kRouteBlocks * 64;         // threads of one key half
+    constexpr int DB = D / 16;                    // 16-dimension blocks of the output
+    constexpr int DC = D / 32;                    // 32-dimension chunks of the scores
+    using St = Stager<D, KSUB, PT>;               // K and V rows padded as there
+    constexpr int MERGE_BYTES = kRouteBlocks * 3 * 16 * (D + 2) * 4;
+    constexpr int SMEM = kRouteParts * 2 * St::STAGE > MERGE_BYTES ? kRouteParts * 2 * St::STAGE : MERGE_BYTES;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const Geo& g = a.g;
     const int N = g.N;
-    const int c0 = chunk * a.chunk;
-    const int c1 = imin(N, c0 + a.chunk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, h = lane >> 5;
-    const int x = __builtin_amdgcn_readfirstlane(wave % 3);   // softmax kind of this wave (wave-uniform)
+    const int part = wave / kRouteBlocks, sb = wave - part * kRouteBlocks;
+    const int ptid = tid - part * PT;
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int sub = a.chunk / kRouteParts;             // a multiple of KSUB
+    const int c0 = chunk * a.chunk + part * sub;
+    const int c1 = imin(N, c0 + sub);                  // keys of this half: [c0, c1), possibly empty
+    const int steps = sub / KSUB;                      // the same for every wave: equal barrier counts
+    char* sm = smem + part * 2 * St::STAGE;
     const size_t head_off = (size_t)bh * N * D;
     const uint16_t* kh = a.k + head_off;
     const uint16_t* vh = a.v + head_off;
 
-    const int n = (wave / 3) * 32 + l32;              // sample slot of this lane
+    const int n = sb * 16 + l16;                       // sample slot of this lane
     int qtok = a.idx[imin(n, a.ns - 1)];
     qtok = imin(imax(qtok, 0), N - 1);
-    bf16x8 qreg[DC];
+    bf16x8 qreg[DC];   // B operand: dims 32 c + 8 grp .. +7 of the sample
     {
-        const bf16x8* p = reinterpret_cast<const bf16x8*>(a.q + head_off + (size_t)qtok * D + 8 * h);
+        const uint16_t* p = a.q + head_off + (size_t)qtok * D + 8 * grp;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qreg[c] = p[2 * c];
+        for (int c = 0; c < DC; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(p + 32 * c);
     }
     const RowKeys rks = row_keys(g, SVGA_KIND_SPATIAL, qtok);   // frame-major = spatial order
     uint32_t fq, sq;
     g.divS.divmod((uint32_t)qtok, fq, sq);
 
-    f32x16 oacc[DB];
+    f32x4 oacc[3][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float mrow = -INFINITY, lrow = 0.f;
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[x][db] = f32x4{};
+    float base = -INFINITY;
+    float lsum[3] = {0.f, 0.f, 0.f};
 
-    const int steps = (c1 - c0 + KSUB - 1) / KSUB;
-    St st;
+    // K / V copy. With few chunks per thread, two register sets, so that the
+    // loads of step t are issued two steps before step t - 1 stores them to
+    // LDS (set t % 2 holds step t); otherwise one set, loaded one step ahead.
+    constexpr bool DEEP = St::CU <= 2;
+    constexpr int AHEAD = DEEP ? 3 : 2;
+    St st0, st1;
     auto ident = [](int j) { return j; };
     if (steps > 0) {
-        st.load(kh, vh, c0, N, ident, tid);
-        st.store(smem, tid);
-        if (steps > 1) st.load(kh, vh, c0 + KSUB, N, ident, tid);
+        st0.load(kh, vh, c0, N, ident, ptid);
+        st0.store(sm, ptid);
+        if (steps > 1) (DEEP ? st1 : st0).load(kh, vh, c0 + KSUB, N, ident, ptid);
+        if (DEEP && steps > 2) st0.load(kh, vh, c0 + 2 * KSUB, N, ident, ptid);
     }
     __syncthreads();
 
-    // 64-bit keep mask over keys kb0 .. kb0+63 for this lane's sample under softmax kind X
-    // (frame-major coordinates), keys at or past the chunk end excluded
-    auto keep_bits = [&](auto X, int kb0) __attribute__((always_inline)) {
-        uint64_t m = window_bits(kb0, c1, kb0);
-        if constexpr (decltype(X)::value == 1) {
-            m &= window_bits(rks.a0, rks.b0, kb0) | window_bits(rks.a1, rks.b1, kb0);
-        } else if constexpr (decltype(X)::value == 2) {
-            // sink frames whole; in every other frame the positions within bt of the sample's
-            uint64_t t = 0;
-            const int f0 = kb0 / g.S, f1 = imin((kb0 + KSUB - 1) / g.S, g.F - 1);
-            for (int f = f0; f <= f1; ++f) {
-                const int fs = f * g.S;
-                t |= f < g.k ? window_bits(fs, fs + g.S, kb0)
-                             : window_bits(fs + imax((int)sq - g.bt, 0), fs + imin((int)sq + g.bt + 1, g.S), kb0);
-            }
-            m &= t;
+    // temporal keep mask over the 32 keys base .. base+31: sink frames whole,
+    // in every other frame the positions within bt of the sample's
+    const int tlo = imax((int)sq - g.bt, 0), thi = imin((int)sq + g.bt + 1, g.S);
+    auto temporal_bits = [&](int base_key) __attribute__((always_inline)) {
+        uint32_t t = 0;
+        const int f0 = (int)g.divS.div((uint32_t)base_key);
+        const int f1 = imin((int)g.divS.div((uint32_t)(base_key + 31)), g.F - 1);
+        for (int f = f0; f <= f1; ++f) {
+            const int fs = f * g.S;
+            t |= f < g.k ? window_bits32(fs, fs + g.S, base_key) : window_bits32(fs + tlo, fs + thi, base_key);
         }
-        return m;
+        return t;
     };
-    auto run = [&](auto X) __attribute__((always_inline)) {
-        for (int s = 0; s < steps; ++s) {
-            const char* stg = smem + (s & 1) * St::STAGE;
-            const int kb0 = c0 + s * KSUB;
-            f32x16 sacc[KBLK];
+    // per-lane LDS offsets: K row l16 of the two score chains (16 consecutive
+    // rows per read, conflict-free with the padded rows); V^T operand (dims
+    // 16 db + 4 (l16 % 4) .. +3 of key 4 grp + l16 / 4, and 16 keys on)
+    const int koff0 = l16 * St::KROW + grp * 16, koff1 = koff0 + 16 * St::KROW;
+    const int voff = St::KBYTES + (4 * grp + (l16 >> 2)) * St::VROW + (l16 & 3) * 8;
+    auto step = [&](const int s, St& nxt) __attribute__((always_inline)) {
+        const char* stg = sm + (s & 1) * St::STAGE;
+        const int kb0 = c0 + s * KSUB;
+        f32x4 sc0 = f32x4{}, sc1 = f32x4{};
 #pragma unroll
-            for (int b = 0; b < KBLK; ++b) sacc[b] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < DC; ++c)
-#pragma unroll
-                for (int b = 0; b < KBLK; ++b)
-                    sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(St::a_k(stg, b, c, l32, h), qreg[c], sacc[b], 0, 0, 0);
-
-            // mask by a bit test per score: bit acc_key(b, i, 0) - 32 b of word b, after a shift
-            // that puts this half-wave's keys at acc_key(b, i, 0)
-            const uint64_t m = keep_bits(X, kb0) >> acc_key(0, 0, h);
-            const uint32_t mw[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
-            float mx = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < KBLK; ++b) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int pos = acc_key(b, i, 0) - 32 * b;
-                    if (!((mw[b] >> pos) & 1u)) sacc[b][i] = -INFINITY;
-                    mx = fmaxf(mx, sacc[b][i]);
-                }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrow, mx);
-            const float base = mnew == -INFINITY ? 0.f : mnew * a.c2;
-            const float alpha = __builtin_amdgcn_exp2f(mrow * a.c2 - base);
-            mrow = mnew;
-            lrow *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-            const int vlo = St::v_lane_off(lane);
-#pragma unroll
-            for (int m16 = 0; m16 < KSUB / 16; ++m16) {
-                // registers 8*(m16%2) .. +7 of key block m16/2 hold keys 16*m16 + 8h .. +7
-                bf16x8 hi8, lo8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[m16 >> 1][8 * (m16 & 1) + e], a.c2, -base));
-                    lrow += p;
-                    const __bf16 ph = (__bf16)p;
-                    hi8[e] = ph;
-                    lo8[e] = (__bf16)(p - (float)ph);
-                }
-                bf16x8 av[DB];
-#pragma unroll
-                for (int db = 0; db < DB; ++db) av[db] = St::a_v(stg, db, m16, vlo);
-                // the high parts of all dimension blocks, then the low parts: no product
-                // waits on the one just before it
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], hi8, oacc[db], 0, 0, 0);
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[db], lo8, oacc[db], 0, 0, 0);
-            }
-
-            if (s + 1 < steps) {
-                st.store(smem + ((s + 1) & 1) * St::STAGE, tid);
-                if (s + 2 < steps) st.load(kh, vh, kb0 + 2 * KSUB, N, ident, tid);
-            }
-            __syncthreads();
+        for (int c = 0; c < DC; ++c) {
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(stg + koff0 + c * 64);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(stg + koff1 + c * 64);
+            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c], sc0, 0, 0, 0);
+            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c], sc1, 0, 0, 0);
         }
-    };
-    // the kind is uniform per wave, so each wave runs one specialised loop (all pass the same barriers)
-    if (x == 0) run(std::integral_constant<int, 0>{});
-    else if (x == 1) run(std::integral_constant<int, 1>{});
-    else run(std::integral_constant<int, 2>{});
+        // the V^T operands of this step, read now so that the softmax below hides their latency
+        bf16x8 av[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const char* vp = stg + voff + db * 32;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * St::VROW));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            av[db] = __builtin_bit_cast(bf16x8, both);
+        }
+        // this lane's scores: element e < 4 is key kb0 + 4 grp + e, e >= 4 key kb0 + 12 + 4 grp + e
+        float sc[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+        const bool whole = kb0 + KSUB <= c1;   // wave-uniform: every key of the step is in the half
+        // bits of this lane's 8 keys, in element order, of a mask over keys kb0 .. kb0+31
+        auto mine = [&](uint32_t m) __attribute__((always_inline)) {
+            return ((m >> (4 * grp)) & 0xfu) | (((m >> (16 + 4 * grp)) & 0xfu) << 4);
+        };
+        uint32_t bs = mine(window_bits32(rks.a0, rks.b0, kb0) | window_bits32(rks.a1, rks.b1, kb0));
+        uint32_t bt = mine(temporal_bits(kb0));
+        float mx = -INFINITY;
+        if (whole) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        } else {
+            const uint32_t bd = mine(window_bits32(kb0, c1, kb0));
+            bs &= bd;
+            bt &= bd;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!((bd >> e) & 1u)) sc[e] = -INFINITY;
+                mx = fmaxf(mx, sc[e]);
+            }
+        }
+        mx = group_max(mx);
+        // a new base when this step's max exceeds the current one by more than 2^8
+        const float cand = mx * a.c2;
+        const bool grow = cand > base + kRouteRescaleLog2;
+        if (__any(grow)) {
+            // rare after a sample's first steps: kept as a branch (the empty asm
+            // stops the compiler from turning it into unconditional multiplies)
+            asm volatile("" ::: "memory");
+            const float nb = grow ? cand : base;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(base - nb) : 1.0f;   // 0 when base is -inf
+            base = nb;
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                lsum[x] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[x][db] *= alpha;
+            }
+        }
+        const float nbase = base == -INFINITY ? 0.f : -base;
+        float p[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], a.c2, nbase));
+            psum += p[e];
+        }
+        // dense P^T: bf16 high parts and bf16 remainders, packed in pairs
+        uint32_t hd[4], ld[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hd[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+            ld[j] = pack_bf16(p[2 * j] - __builtin_bit_cast(float, hd[j] << 16),
+                              p[2 * j + 1] - __builtin_bit_cast(float, hd[j] & 0xffff0000u));
+        }
+        lsum[0] += psum;
+        // masked P^T: the dense pairs with excluded keys zeroed. Usually every lane
+        // keeps all or none of its 8 keys under each mask (a range boundary falls
+        // inside few of them): then whole pairs are selected
+        uint32_t hs[4], ls[4], ht[4], lt[4];
+        if (__all((bs == 0u || bs == 0xffu) && (bt == 0u || bt == 0xffu))) {
+            const uint32_t ms = bs ? ~0u : 0u, mt = bt ? ~0u : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hs[j] = hd[j] & ms;
+                ls[j] = ld[j] & ms;
+                ht[j] = hd[j] & mt;
+                lt[j] = ld[j] & mt;
+            }
+            lsum[1] += bs ? psum : 0.f;
+            lsum[2] += bt ? psum : 0.f;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t ms = pair_mask(bs, j), mt = pair_mask(bt, j);
+                hs[j] = hd[j] & ms;
+                ls[j] = ld[j] & ms;
+                ht[j] = hd[j] & mt;
+                lt[j] = ld[j] & mt;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lsum[1] += ((bs >> e) & 1u) ? p[e] : 0.f;
+                lsum[2] += ((bt >> e) & 1u) ? p[e] : 0.f;
+            }
+        }
+        const bf16x8 ph[3] = {as_bf16x8(hd), as_bf16x8(hs), as_bf16x8(ht)};
+        const bf16x8 pl[3] = {as_bf16x8(ld), as_bf16x8(ls), as_bf16x8(lt)};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], ph[x], oacc[x][db], 0, 0, 0);
+#pragma unroll
+            for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pl[x], oacc[x][db], 0, 0, 0);
+        }
 
-    // ---- partial of this (sample, kind): max in the log2 domain, sum, unnormalised output
-    const float lt = lrow + __shfl_xor(lrow, 32);
-    float* w = a.ws + ws_index<D>(bh, chunk, a.n_chunks, x, n);
-    if (h == 0) {
-        w[0] = mrow == -INFINITY ? -INFINITY : mrow * a.c2;
-        w[1] = lt;
+        // nxt holds step s+1: to LDS, then refill it with step s+AHEAD
+        if (s + 1 < steps) {
+            nxt.store(sm + ((s + 1) & 1) * St::STAGE, ptid);
+            if (s + AHEAD < steps) nxt.load(kh, vh, kb0 + AHEAD * KSUB, N, ident, ptid);
+        }
+        __syncthreads();
+    };
+    for (int s = 0; s < steps; s += 2) {
+        step(s, DEEP ? st1 : st0);
+        if (s + 1 < steps) step(s + 1, st0);
     }
+
+    // ---- the two key halves of each sample block merge in LDS; half 0 writes the partial
+    float lt3[3];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int x = 0; x < 3; ++x) lt3[x] = group_sum(lsum[x]);
+    float* mrg = reinterpret_cast<float*>(smem) + (size_t)sb * 3 * 16 * (D + 2);   // [x][l16][D + 2]
+    if (part == 1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[2 + db * 32 + 8 * (i >> 2) + 4 * h + (i & 3)] = oacc[db][i];
+        for (int x = 0; x < 3; ++x) {
+            float* w = mrg + ((size_t)x * 16 + l16) * (D + 2);
+            if (grp == 0) {
+                w[0] = base;
+                w[1] = lt3[x];
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[2 + db * 16 + 4 * grp + r] = oacc[x][db][r];
+        }
+    }
+    __syncthreads();
+    if (part == 0) {
+        const float b1 = mrg[(size_t)l16 * (D + 2)];
+        const float m = fmaxf(base, b1);
+        const float s0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(base - m);
+        const float s1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(b1 - m);
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const float* w1 = mrg + ((size_t)x * 16 + l16) * (D + 2);
+            float* w = a.ws + ws_index<D>(bh, chunk, a.n_chunks, x, n);
+            if (grp == 0) {
+                w[0] = m;
+                w[1] = lt3[x] * s0 + w1[1] * s1;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = db * 16 + 4 * grp + r;
+                    w[2 + d] = oacc[x][db][r] * s0 + w1[2 + d] * s1;
+                }
+        }
+    }
 }
 
 // One workgroup (D threads) per (sample, batch*head): merge the chunk partials
@@ -307,9 +485,10 @@ __global__ void route_flag_kernel(RArgs a, int BH) {
     }
 }
 
-template <int D, int QBLK, int KSUB>
+template <int D>
 hipError_t launch_pair(const RArgs& r, int BH, hipStream_t stream) {
-    hipLaunchKernelGGL((route_partial_kernel<D, QBLK, KSUB>), dim3(r.n_chunks, BH), dim3(QBLK * 3 * 64), 0, stream, r);
+    hipLaunchKernelGGL((route_partial_kernel<D>), dim3(r.n_chunks, BH), dim3(kRouteBlocks * kRouteParts * 64), 0,
+                       stream, r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_merge_kernel<D>), dim3(r.ns, BH), dim3(D), 0, stream, r);
@@ -320,24 +499,6 @@ hipError_t launch_pair(const RArgs& r, int BH, hipStream_t stream) {
 }
 
 }  // namespace
-
-void route_plan(int32_t BH, int32_t N, int32_t head_dim, int32_t n_samples, int32_t* chunk, int32_t* n_chunks,
-                size_t* ws_bytes) {
-    (void)n_samples;
-    // About 512 workgroups in all, chunks a multiple of 64 keys. Fewer, longer
-    // chunks keep the partials small (each chunk writes 3 x 64 rows of D + 2
-    // floats per head, which the merge reads back), more chunks spread the
-    // pass better: measured fastest among 256 .. 2048 workgroups at 75,600
-    // and 302,400 tokens (at 75,600: 256 -> 0.29 ms, 384 -> 0.22, 512 -> 0.19,
-    // 768 -> 0.20 for the partial pass).
-    int64_t target = ((int64_t)N * BH + 511) / 512;
-    int64_t c = (target + 63) / 64 * 64;
-    if (c < 256) c = 256;
-    *chunk = (int32_t)c;
-    *n_chunks = (int32_t)((N + c - 1) / c);
-    *ws_bytes = ((size_t)BH * (size_t)*n_chunks * 3 * kMaxSamples * (size_t)(head_dim + 2) +
-                 (size_t)BH * kMaxSamples * 2) * sizeof(float);
-}
 
 hipError_t launch_route(const RouteLaunch& a, hipStream_t stream) {
     RArgs r;
@@ -354,9 +515,9 @@ hipError_t launch_route(const RouteLaunch& a, hipStream_t stream) {
     r.ws_err = r.ws + (size_t)a.BH * a.n_chunks * 3 * kMaxSamples * (a.head_dim + 2);
     r.flags = a.flags;
     r.err = a.err;
-    const bool two = a.n_samples > 32;
-    if (a.head_dim == 64) return two ? launch_pair<64, 2, 64>(r, a.BH, stream) : launch_pair<64, 1, 64>(r, a.BH, stream);
-    return two ? launch_pair<128, 2, 64>(r, a.BH, stream) : launch_pair<128, 1, 64>(r, a.BH, stream);
+    // every call runs four 16-sample blocks (slots past n_samples repeat the last sample)
+    if (a.head_dim == 64) return launch_pair<64>(r, a.BH, stream);
+    return launch_pair<128>(r, a.BH, stream);
 }
 
 }  // namespace svga

@@ -257,6 +257,7 @@ inline size_t attn_split_workspace_bytes(int32_t head_dim, int32_t bq) {
     if (bq < 32 * kSplitWaves) return kAttnWorkspaceBytes;   // no split below 256-row workgroups
     return kSplitLseOffset + split_lse_bytes(bq) + kSplitItemsMax * kSplitParts * split_rows(bq) * head_dim * 2;
 }
+// Tile shapes with a compiled attention kernel (plan_host.cpp).
 bool attn_supported(int32_t head_dim, int32_t bq, int32_t bkv);
 // Scratch of svga_sparse_attn_fwd_noalloc: the split-tail workspace of the
 // largest supported case (head_dim 128, 256-row workgroups), 68,157,696 bytes.
@@ -285,9 +286,17 @@ struct RouteLaunch {
     uint8_t* flags;
     float* err;
 };
+// Routing runs 64 sample slots per head (slots past n_samples repeat the last sample).
+constexpr int kRouteMaxSamples = 64;
+// Key chunking and workspace bytes of a routing call (plan_host.cpp).
 void route_plan(int32_t BH, int32_t N, int32_t head_dim, int32_t n_samples, int32_t* chunk, int32_t* n_chunks,
                 size_t* ws_bytes);
 hipError_t launch_route(const RouteLaunch& a, hipStream_t stream);
+
+// Kept pairs of a whole head and the band for a target kept fraction (plan_host.cpp).
+int64_t kept_pairs_spatial(int32_t F, int64_t S, int32_t sink, int32_t band);
+int64_t kept_pairs_temporal(int32_t F, int64_t S, int32_t sink, int32_t band);
+int32_t band_for_kept_fraction(int32_t kind, int32_t F, int64_t S, int32_t sink, double target);
 
 // Host builder (tilemap_host.cpp).
 void build_tilemap_host(const Geo& g, int32_t bq, int32_t bkv, int32_t mode, unsigned char* h_map,

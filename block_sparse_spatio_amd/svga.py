@@ -96,6 +96,15 @@ def svga_version():
     return lib().svga_version()
 
 
+def svga_mask_for_kept_fraction(geom, sink_frames, spatial_target, temporal_target, temporal_layout=TL_SINK_FIRST):
+    """(mask, (kept_spatial, kept_temporal)): the smallest bands whose kept pairs per head reach the targets."""
+    m = SvgaMask()
+    kept = (ctypes.c_int64 * 2)()
+    _check(lib().svga_mask_for_kept_fraction(ctypes.byref(_geom(geom)), int(sink_frames), int(temporal_layout),
+                                             float(spatial_target), float(temporal_target), ctypes.byref(m), kept))
+    return m, (int(kept[0]), int(kept[1]))
+
+
 def svga_tilemap_layout(geom, bq, bkv):
     off = SvgaTilemapOffsets()
     _check(lib().svga_tilemap_layout(ctypes.byref(_geom(geom)), int(bq), int(bkv), ctypes.byref(off)))

@@ -83,6 +83,25 @@ typedef struct svga_mask {
     int32_t temporal_layout;
 } svga_mask;
 
+/* Mask for target kept fractions: the sparsity knob of ASTA section
+ * "End-to-end results and takeaways" (Table 3 compares schedules that keep
+ * progressively fewer attention pairs; a schedule picks, per denoising step
+ * and layer, how many pairs each head kind keeps).
+ * Fills *out with sink_frames, temporal_layout and, for each kind, the
+ * smallest band whose kept pairs of one head, counted in closed form from
+ * the mask definitions above (spatial: frames; temporal: flattened
+ * positions), reach target * N^2. The comparison is exact: a double target
+ * is a dyadic rational, and the count it needs is formed in 128-bit integer
+ * arithmetic. Bands run from 0 up to the first that keeps every pair
+ * (F - 1, resp. H*W - 1), so a target at or below a kind's band-0 fraction
+ * gives band 0 and a target of 1 gives the dense mask.
+ * spatial_target, temporal_target: in [0, 1] (SVGA_EINVAL otherwise, NaN
+ * included). kept_pairs: host int64[2] receiving the chosen masks' kept pairs
+ * per head (spatial, temporal), or NULL. Host only; no device work. */
+svga_status svga_mask_for_kept_fraction(const svga_geom* geom, int32_t sink_frames, int32_t temporal_layout,
+                                        double spatial_target, double temporal_target,
+                                        svga_mask* out, int64_t* kept_pairs);
+
 /* ---------------------------------------------------------------- tile map */
 
 /* Traversals of ASTA Figure 4 / Table 2.

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == len(_lib.SIGNATURES) == 15
+    assert len(names) == len(_lib.SIGNATURES) == 16
     assert set(names) == set(_lib.SIGNATURES)
     for n in names:
         assert hasattr(L, n), n
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.svga_version() == 103
+    assert L.svga_version() == 104
     assert L.svga_status_string(0) == b"ok"
     assert L.svga_status_string(-3) == b"buffer too small"
 

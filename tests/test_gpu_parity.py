@@ -180,6 +180,26 @@ def test_attention_small(dev, tiles, mode):
         assert_close(o[0, h, rows].float().numpy(), ref, f"head {h}")
 
 
+@pytest.mark.parametrize("level", [0, 1, 2])
+def test_schedule_levels_small(dev, level):
+    """Each level of a three-level sparsity schedule (masks from svga_mask_for_kept_fraction) at Small, 128x128."""
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    sched = B.SparsitySchedule(geom, [(0, 0.7, 0.6), (10, 0.5, 0.4), (20, 0.3, 0.2)], sink_frames=w.sink_frames,
+                               temporal_layout=w.temporal_layout)
+    p = sched.plan(10 * level, 1)
+    mask = (p.mask.sink_frames, p.mask.spatial_band, p.mask.temporal_band, p.mask.temporal_layout)
+    say(f"schedule level {level}: mask {mask}, kept pairs {p.kept_pairs} of {w.N ** 2}")
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=11 + level)
+    o, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, 128, 128, p.mode)
+    rows = np.sort(np.random.default_rng(level).choice(w.N, 256, replace=False))
+    rows = np.unique(np.concatenate([rows, np.arange(64), np.arange(w.N - 64, w.N)]))
+    for h, kind in enumerate(w.kinds):
+        ref, _ = oracle_head(geom, mask, q[0, h], k[0, h], v[0, h], kind, p.mode, 128, 128, 1 / math.sqrt(w.d),
+                             rows=rows)
+        assert_close(o[0, h, rows].float().numpy(), ref, f"head {h}")
+
+
 @pytest.mark.parametrize("tiles,mode,gather", [((256, 128), 2, False), ((256, 128), 3, True), ((512, 128), 2, False),
                                                ((128, 64), 0, False), ((32, 32), 1, False), ((256, 96), 2, True)])
 def test_persistent_equals_plain_bitwise(dev, tiles, mode, gather):
