@@ -173,6 +173,15 @@ def main():
         extras["permute_path_ms (3 permutes + attention + unpermute)"] = round(3 * t_perm + t_attn + t_unperm, 4)
         for bq_x in (128, 256, 512):
             extras[f"exact_bq{bq_x}_ms"] = round(attn_with(B.MAP_EXACT, bq_x), 4)
+        # balanced rounding (B3): temporal heads through the permutations or read in place by the kernel
+        for bq_x in (128, 256):
+            t_r = attn_with(B.MAP_ROUNDED, bq_x)
+            extras[f"rounded_{bq_x}x{bkv}"] = {
+                "attn_ms": round(t_r, 4),
+                "permute_path_ms (3 permutes + attention + unpermute)": round(3 * t_perm + t_r + t_unperm, 4),
+                "gather_ms (attention reading temporal heads in place)": round(
+                    attn_with(B.MAP_ROUNDED, bq_x, gather=True), 4)}
+        extras["small_3456"] = small_dense_vs_sparse(B, torch, dev, aws, timed, reps)
         extras["layer_1440p"] = layer_1440p(B, torch, dev, P1440, aws)
 
     cpu = None
@@ -244,6 +253,30 @@ def main():
         "context_tpu_v6e_ms (pages, isolated kernel, other hardware)": PAGES_TPU_V6E_MS,
     }
     print(json.dumps(out), flush=True)
+
+
+def small_dense_vs_sparse(B, torch, dev, aws, timed, reps):
+    """The 3,456-token case (9x16x24, 4 heads: 2 spatial, 2 temporal, d=128, 128x128 tiles): exact sparse
+    attention against the dense map on the same permuted inputs (attention call only)."""
+    from synth import SMALL, normal_qkv
+    w = SMALL
+    geom = (w.F, w.H, w.W)
+    mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
+    q, k, v = (x.to(dev) for x in normal_qkv(1, w.heads, w.N, w.d, seed=1))
+    flags = torch.tensor([list(w.kinds)], dtype=torch.uint8, device=dev)
+    qp, kp, vp = (B.svga_permute(x, flags, geom, mask) for x in (q, k, v))
+    op = torch.empty_like(qp)
+    res = {"workload": "3,456 tokens (9x16x24), 4 heads (2 spatial band 1, 2 temporal window 24), d=128, 128x128"}
+    for name, mode in (("exact", B.MAP_EXACT), ("dense", B.MAP_DENSE)):
+        m = B.svga_build_tilemap(geom, mask, w.bq, w.bkv, mode, device=dev)
+        t = timed(lambda: B.svga_sparse_attn_fwd(qp, kp, vp, flags, m, geom, mask, w.bq, w.bkv, mode, out=op,
+                                                 workspace=aws), reps)
+        hm = B.tilemap_views(m.cpu().numpy(), geom, w.bq, w.bkv)
+        n_exec = int(sum(hm["n_full"][kk].sum() + hm["n_bnd"][kk].sum() for kk in w.kinds))
+        res[f"{name}_ms"] = round(t, 4)
+        res[f"{name}_executed_tile_tflops"] = round(4.0 * w.d * w.bq * w.bkv * n_exec / (t * 1e-3) / 1e12, 1)
+    res["speedup_exact_vs_dense"] = round(res["dense_ms"] / res["exact_ms"], 3)
+    return res
 
 
 def layer_1440p(B, torch, dev, w, aws):

@@ -3,7 +3,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsvga.so")
+# SVGA_LIBRARY names another build of the same ABI (the tests' host-only sanitizer build uses it)
+LIB_PATH = os.environ.get("SVGA_LIBRARY") or os.path.join(HERE, "libsvga.so")
 
 c_i32 = ctypes.c_int32
 c_size = ctypes.c_size_t
