@@ -76,26 +76,23 @@ __device__ __forceinline__ uint32_t window_bits32(int a, int b, int base) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// The other values of x among the four lanes l % 16 + 16 j (lane-row swaps
-// of v_permlane16_swap and v_permlane32_swap: each returns the partner row's
-// value in one of its two results, whichever lane calls it).
-__device__ __forceinline__ float swap16(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __builtin_bit_cast(float, (uint32_t)r[0] == u ? (uint32_t)r[1] : (uint32_t)r[0]);
-}
-__device__ __forceinline__ float swap32(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __builtin_bit_cast(float, (uint32_t)r[0] == u ? (uint32_t)r[1] : (uint32_t)r[0]);
-}
+// Reductions over the four lanes l % 16 + 16 j. v_permlane16_swap of x with
+// itself leaves, in every lane, the values of rows 2i and 2i+1 (16-lane rows)
+// of its pair of rows in its two results; v_permlane32_swap the same for the
+// two 32-lane halves. Combining the two results of each swap reduces a level.
 __device__ __forceinline__ float group_max(float x) {
-    x = fmaxf(x, swap16(x));
-    return fmaxf(x, swap32(x));
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    u = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+    const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)t[0]), __builtin_bit_cast(float, (uint32_t)t[1]));
 }
 __device__ __forceinline__ float group_sum(float x) {
-    x += swap16(x);
-    return x + swap32(x);
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    u = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+    const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)t[0]) + __builtin_bit_cast(float, (uint32_t)t[1]);
 }
 
 // Two bf16 (round to nearest even) packed in one word, x in the low half.
@@ -135,7 +132,10 @@ void route_partial_kernel(RArgs a) {
     constexpr int PT = kRouteBlocks * 64;         // threads of one key half
     constexpr int DB = D / 16;                    // 16-dimension blocks of the output
     constexpr int DC = D / 32;                    // 32-dimension chunks of the scores
-    using St = Stager<D, KSUB, PT>;               // K and V rows padded as there
+    // K rows padded as in the attention kernel; V rows 32 bytes past a
+    // multiple of 256, so that the 8 rows of keys 0..7 (one half-wave's
+    // transposing read below) start 8 banks apart and never share a bank
+    using St = Stager<D, KSUB, PT, 32>;
     constexpr int MERGE_BYTES = kRouteBlocks * 3 * 16 * (D + 2) * 4;
     constexpr int SMEM = kRouteParts * 2 * St::STAGE > MERGE_BYTES ? kRouteParts * 2 * St::STAGE : MERGE_BYTES;
     __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -143,7 +143,9 @@ void route_partial_kernel(RArgs a) {
     const int chunk = blockIdx.x, bh = blockIdx.y;
     const Geo& g = a.g;
     const int N = g.N;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index through readfirstlane, so that everything derived from it
+    // (key half, step keys, frame ranges) is known wave-uniform and kept in SGPRs
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int part = wave / kRouteBlocks, sb = wave - part * kRouteBlocks;
     const int ptid = tid - part * PT;
     const int l16 = lane & 15, grp = lane >> 4;
@@ -232,29 +234,41 @@ void route_partial_kernel(RArgs a) {
             const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             av[db] = __builtin_bit_cast(bf16x8, both);
         }
-        // this lane's scores: element e < 4 is key kb0 + 4 grp + e, e >= 4 key kb0 + 12 + 4 grp + e
-        float sc[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
         const bool whole = kb0 + KSUB <= c1;   // wave-uniform: every key of the step is in the half
         // bits of this lane's 8 keys, in element order, of a mask over keys kb0 .. kb0+31
         auto mine = [&](uint32_t m) __attribute__((always_inline)) {
-            return ((m >> (4 * grp)) & 0xfu) | (((m >> (16 + 4 * grp)) & 0xfu) << 4);
+            return __builtin_amdgcn_ubfe(m, 4 * grp, 4) | (__builtin_amdgcn_ubfe(m, 16 + 4 * grp, 4) << 4);
         };
-        uint32_t bs = mine(window_bits32(rks.a0, rks.b0, kb0) | window_bits32(rks.a1, rks.b1, kb0));
-        uint32_t bt = mine(temporal_bits(kb0));
-        float mx = -INFINITY;
-        if (whole) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        // Keep bits of the lane's keys. Usually the step lies in one frame f0
+        // (wave-uniform): the spatial mask keeps the whole frame or none of it,
+        // and the temporal one the sample's window within it, or all of a sink
+        // frame. A step across frames takes the general ranges.
+        const int f0 = (int)g.divS.div((uint32_t)kb0);
+        uint32_t bs, bt;
+        if (f0 == (int)g.divS.div((uint32_t)(kb0 + KSUB - 1))) {
+            bs = f0 < g.k || abs(f0 - (int)fq) <= g.bs ? 0xffu : 0u;
+            bt = f0 < g.k ? 0xffu : mine(window_bits32(f0 * g.S + tlo, f0 * g.S + thi, kb0));
         } else {
+            bs = mine(window_bits32(rks.a0, rks.b0, kb0) | window_bits32(rks.a1, rks.b1, kb0));
+            bt = mine(temporal_bits(kb0));
+        }
+        if (!whole) {
+            // the step runs over the end of the half (rare): its keys past the end
+            // get a score of -inf, so that no softmax keeps them
             const uint32_t bd = mine(window_bits32(kb0, c1, kb0));
             bs &= bd;
             bt &= bd;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (!((bd >> e) & 1u)) sc[e] = -INFINITY;
-                mx = fmaxf(mx, sc[e]);
+            for (int e = 0; e < 4; ++e) {
+                sc0[e] = (bd >> e) & 1u ? sc0[e] : -INFINITY;
+                sc1[e] = (bd >> (4 + e)) & 1u ? sc1[e] : -INFINITY;
             }
         }
+        // this lane's scores: element e < 4 is key kb0 + 4 grp + e, e >= 4 key kb0 + 12 + 4 grp + e
+        const float sc[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[e]);
         mx = group_max(mx);
         // a new base when this step's max exceeds the current one by more than 2^8
         const float cand = mx * a.c2;
@@ -281,7 +295,9 @@ void route_partial_kernel(RArgs a) {
             p[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], a.c2, nbase));
             psum += p[e];
         }
-        // dense P^T: bf16 high parts and bf16 remainders, packed in pairs
+        // dense P^T: bf16 high parts and bf16 remainders, packed in pairs (a
+        // bf16 P alone, even with the sums taken over the rounded weights,
+        // leaves the errors of a one-sample route 1.2e-3 off)
         uint32_t hd[4], ld[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

@@ -47,13 +47,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* p, int b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
-template <int D, int KSUB, int NT>
+// VPAD: V row padding in bytes (64 suits a_v's lane layout; other read
+// patterns pick their own).
+template <int D, int KSUB, int NT, int VPAD = 64>
 struct Stager {
     static constexpr int RV = D / 8;                 // 16-byte chunks per row
     static constexpr int CH = KSUB * RV;             // chunks per tensor per sub-tile
     static constexpr int CU = (CH + NT - 1) / NT;    // chunks per thread per tensor
     static constexpr int KROW = D * 2 + 16;          // padded K row (bytes)
-    static constexpr int VROW = D * 2 + 64;          // padded V row (bytes)
+    static constexpr int VROW = D * 2 + VPAD;        // padded V row (bytes)
     static constexpr int KBYTES = KSUB * KROW;
     static constexpr int STAGE = KBYTES + KSUB * VROW;   // K tile, then V tile
 

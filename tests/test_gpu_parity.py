@@ -458,6 +458,7 @@ def check_routing(dev, geom, mask, q, k, v, idx, tol=1e-3):
     f = flags.cpu().numpy()
     say(f"  err gpu {e.reshape(-1, 2)[:4].tolist()} oracle {e_ref.reshape(-1, 2)[:4].tolist()}")
     big = np.maximum(e_ref.max(axis=-1, keepdims=True), 1e-30)
+    say(f"  max relative error {(np.abs(e - e_ref) / big).max():.3e} (bar {tol:g})")
     assert (np.abs(e - e_ref) <= tol * big).all()
     decided = np.abs(e_ref[..., 1] - e_ref[..., 0]) > tol * big[..., 0]
     assert np.array_equal(f[decided], f_ref[decided])
