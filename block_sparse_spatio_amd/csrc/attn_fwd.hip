@@ -317,11 +317,13 @@ struct Step {
     }
 };
 
-// Workgroup barrier between two phases: no data is handed over through LDS
-// here, and sched_barrier keeps the scheduler from moving work across it.
+// The one workgroup barrier of a ping-pong step, between its two phases: it
+// waits for this wave's LDS writes (the stage that waves 4-7 stored in the
+// phase before it becomes visible), and sched_barrier keeps the scheduler from
+// moving work across it.
 __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
+    __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -465,10 +467,13 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
         // chunk at a time between the blocks of exponentials, so that neither
         // the LDS writes nor the load issue form a burst; waves 0-3 issue no
         // memory traffic in the loop. Step s's products read stages s-1 (V)
-        // and s (K); stage s+1 was last read in step s-2, so the four stages
-        // never overlap a write with a read, and the barrier at the top of step
-        // s+1 publishes stage s+1. Loads past the last step repeat its keys
-        // (never stored where anyone reads).
+        // and s (K); stage s+1 was last read in step s-2, before the barrier
+        // of step s-1, so the four stages never overlap a write with a read,
+        // and the barrier in the middle of step s publishes stage s+1 to the
+        // products of step s+1. That one barrier per step also keeps the two
+        // wave groups half a step apart; a second one at the step top (tried)
+        // only added its wait. Loads past the last step repeat its keys (never
+        // stored where anyone reads).
         auto stage = [&](int s) { return (const char*)(smem + (s & 3) * St::STAGE); };
         auto wstage = [&](int s) { return smem + (s & 3) * St::STAGE; };
         const bool lead = wave < WAVES / 2;   // products first
@@ -483,11 +488,14 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
             sh.store(wstage(0), htid);
             sh.load(kh, vh, key_base(imin(1, steps - 1)), N, src, htid);
         }
-        auto top = [&]() __attribute__((always_inline)) {
+        // step top: a barrier only before the first step (stage 0 from the
+        // prologue), otherwise a scheduling fence
+        auto first_top = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
         };
+        auto top = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
         // gathered rows: the source rows of the keys that step s's transfer loads,
         // found in the matrix phase before it (where VALU time is free): lane i
         // finds the source of key kb + i, each chunk takes its row's from that lane
@@ -546,14 +554,14 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
         using One = std::false_type;
         using Yes = std::true_type;
         using No = std::false_type;
-        // Every wave passes the same 2 * (steps + 1) barriers. The first and
-        // last steps are peeled so that the loops hold one form of each phase.
+        // Every wave passes the same steps + 2 barriers. The first and last
+        // steps are peeled so that the loops hold one form of each phase.
         const int sf = imin(sfull, steps);
         if (steps == 0) {
             __syncthreads();
             phase_barrier();
         } else if (lead) {
-            top();
+            first_top();
             prod(One{}, 0);
             phase_barrier();
             if (0 < sfull) soft(No{}, No{}, 0, 0);
@@ -575,7 +583,7 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
             prod(One{}, steps);
             phase_barrier();
         } else {
-            top();
+            first_top();
             sh.store(wstage(1), htid);
             sh.load(kh, vh, next_keys(0), N, src, htid);
             phase_barrier();
