@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the variant and sweep timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle on whole heads and the whole tile map, routing and permutations "
+                         "(a few minutes) instead of the bounded sample")
     return ap.parse_args()
 
 
@@ -187,7 +190,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle cpu baseline")
-        cpu = cpu_baseline(w, q, k, v, routed, bq, bkv, args.cpu_seconds)
+        cpu = cpu_baseline(w, q, k, v, routed, bq, bkv, args.cpu_seconds, full=args.cpu_full)
 
     out = {
         "metric": METRIC,
@@ -359,8 +362,11 @@ def counted_mfma_busy(mode, bq, bkv):
     return counter_record("attn_fwd_headline_exact_256x128_mfma_counters.md", "mfma_busy_pct", mode, bq, bkv)
 
 
-def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
-    """The oracle, unchanged, on a bounded sample of the step; extrapolated to the whole step."""
+def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s, full=False):
+    """The oracle, unchanged, on a bounded sample of the step; extrapolated to the whole step. With `full`,
+    every query row of one spatial and one temporal head (the other heads of each kind cost the same: the
+    oracle's work depends on the mask, not on the values), the whole tile map, routing of every head on all
+    its samples, and every permutation of the step."""
     import numpy as np
 
     import oracle as O
@@ -379,7 +385,14 @@ def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
     rng = np.random.default_rng(0)
     q0 = {h: (q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy()) for h in (0, 5)}
     n_rows = 64
-    while t_attn < 0.6 * target_s and rows_done < N:
+    if full:
+        for h in (0, 5):
+            t0 = time.perf_counter()
+            O.attention_head(*q0[h], flags[h], w.F, w.H, w.W, *mask, w.temporal_layout, O.MODE_EXACT, bq, bkv,
+                             scale)
+            t_attn += (time.perf_counter() - t0) * sum(1 for f in flags if f == flags[h])
+        rows_done = N * w.heads
+    while not full and t_attn < 0.6 * target_s and rows_done < N:
         for h in (0, 5):
             rows = rng.choice(N, n_rows, replace=False)
             t0 = time.perf_counter()
@@ -388,24 +401,38 @@ def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
             t_attn += time.perf_counter() - t0
             rows_done += n_rows
         n_rows *= 2
-    attn_full = t_attn / rows_done * N * w.heads
+    attn_full = t_attn if full else t_attn / rows_done * N * w.heads
     # tile map: the element scan of a few query tiles per kind
     t0 = time.perf_counter()
-    nq = 4
+    tq = -(-N // bq)
+    nq = tq if full else 4
     for kind in (0, 1):
         O.tile_counts(w.F, w.H, w.W, kind, *mask, w.temporal_layout, bq, bkv, q_tiles=range(nq))
-    tq = -(-N // bq)
     map_full = (time.perf_counter() - t0) / nq * tq
     # routing: 8 of the 64 sampled queries of one head
     t0 = time.perf_counter()
-    O.route_heads(q[:, :1].double().numpy()[:, :, :], k[:, :1].double().numpy(), v[:, :1].double().numpy(),
-                  w.F, w.H, w.W, *mask, np.arange(8) * 997, scale)
-    route_full = (time.perf_counter() - t0) / 8 * w.n_samples * w.heads
+    if full:
+        from synth import sample_indices
+        O.route_heads(q.double().numpy(), k.double().numpy(), v.double().numpy(), w.F, w.H, w.W, *mask,
+                      sample_indices(N, w.n_samples, seed=0).numpy(), scale)
+        route_full = time.perf_counter() - t0
+    else:
+        O.route_heads(q[:, :1].double().numpy()[:, :, :], k[:, :1].double().numpy(), v[:, :1].double().numpy(),
+                      w.F, w.H, w.W, *mask, np.arange(8) * 997, scale)
+        route_full = (time.perf_counter() - t0) / 8 * w.n_samples * w.heads
     # permutation of one head of one tensor
     t0 = time.perf_counter()
     order = O.executed_order(w.F, w.H, w.W, 1, w.sink_frames, w.temporal_layout)
-    O.permute(q[0, 5].float().numpy(), order)
-    perm_full = (time.perf_counter() - t0) * 4 * sum(flags)
+    if full:
+        for h in range(w.heads):
+            if flags[h]:
+                for x in (q, k, v):
+                    O.permute(x[0, h].float().numpy(), order)
+                O.unpermute(q[0, h].float().numpy(), order)
+        perm_full = time.perf_counter() - t0
+    else:
+        O.permute(q[0, 5].float().numpy(), order)
+        perm_full = (time.perf_counter() - t0) * 4 * sum(flags)
     total_s = attn_full + map_full + route_full + perm_full
     return {
         "value": round(total_s * 1e3, 1),
@@ -413,9 +440,12 @@ def cpu_baseline(w, q, k, v, flags, bq, bkv, target_s):
         "cores": blas,
         "host_cpus": cores,
         "kind": "oracle",
-        "sample": f"attention: {rows_done} query rows of heads 0 and 5 (of {N * w.heads}); tile map: {nq} of {tq} "
-                  f"query tiles per kind; routing: 8 of {w.n_samples} samples of 1 of {w.heads} heads; permute: "
-                  "1 head of 1 tensor; each scaled linearly to the full step",
+        "sample": ("whole step: every query row of head 0 (spatial) and head 5 (temporal), each counted once "
+                   "per head of its kind; the whole tile map; routing of all heads on all samples; every "
+                   "permutation" if full else
+                   f"attention: {rows_done} query rows of heads 0 and 5 (of {N * w.heads}); tile map: {nq} of {tq} "
+                   f"query tiles per kind; routing: 8 of {w.n_samples} samples of 1 of {w.heads} heads; permute: "
+                   "1 head of 1 tensor; each scaled linearly to the full step"),
         "measured_s": round(time.perf_counter() - t_begin, 2),
         "parts_ms": {"attention": round(attn_full * 1e3, 1), "tilemap": round(map_full * 1e3, 1),
                      "routing": round(route_full * 1e3, 1), "permute": round(perm_full * 1e3, 1)},
