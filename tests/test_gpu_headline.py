@@ -222,12 +222,16 @@ def test_headline_census(dev, form):
 
 
 def test_headline_gather_equals_permute_bitwise(dev, headline):
+    """The in-kernel gather gives the same bits (output and LSE) as the permute path at full size, in the
+    benchmark's split-tail launch."""
     w, q, k, v, qd, kd, vd = headline
     flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
     say("headline gather vs permute")
-    a = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT)
-    b = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT, gather=True)
+    ws = split_workspace(dev, w, 256)
+    a, la = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT, workspace=ws, want_lse=True)
+    b, lb = pipeline(dev, w, qd, kd, vd, flags, 256, 128, B.MAP_EXACT, gather=True, workspace=ws, want_lse=True)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(la, lb)
 
 
 def test_headline_persistent_equals_plain_bitwise(dev, headline):

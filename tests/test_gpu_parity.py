@@ -341,17 +341,24 @@ def test_binding_rejects_bad_buffers(dev):
 
 
 def test_gather_equals_permute_path_bitwise(dev):
-    """In-kernel gather of temporal rows gives the same bits as permute -> attention -> unpermute."""
+    """In-kernel gather of temporal rows gives the same bits, output and LSE, as permute -> attention ->
+    unpermute; also in the persistent launch with the split tail."""
     w = SMALL
     geom = (w.F, w.H, w.W)
     for lay in (0, 1):
         mask = (w.sink_frames, w.spatial_band, w.temporal_band, lay)
         q, k, v = normal_qkv(2, w.heads, w.N, w.d, seed=2)
-        for bq, bkv, mode in ((128, 128, 2), (256, 128, 3), (64, 64, 1)):
-            say(f"gather layout={lay} tiles={bq}x{bkv} mode={mode}")
-            a, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=False)
-            b, _ = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=True)
+        for bq, bkv, mode, split in ((128, 128, 2, False), (256, 128, 3, True), (64, 64, 1, False),
+                                     (512, 64, 2, True), (256, 96, 2, False)):
+            ws = torch.zeros(B.svga_attn_split_workspace_bytes(w.d, bq), dtype=torch.uint8, device=dev) \
+                if split else None
+            say(f"gather layout={lay} tiles={bq}x{bkv} mode={mode} split={split}")
+            a, la = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=False, want_lse=True,
+                                  workspace=ws)
+            b, lb = run_attention(dev, geom, mask, q, k, v, w.kinds, bq, bkv, mode, gather=True, want_lse=True,
+                                  workspace=ws)
             assert np.array_equal(i16(a), i16(b))
+            assert np.array_equal(la.numpy(), lb.numpy())
 
 
 def test_naive_and_exact_agree(dev):
