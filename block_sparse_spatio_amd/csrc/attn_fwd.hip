@@ -26,15 +26,15 @@
 //   operands come from transposing LDS reads; rows are padded so that all
 //   operand reads are conflict-free (tile_stage.h).
 // * Ping-pong (8-wave workgroups): waves w and w+4 share a SIMD. Each step
-//   has two phases separated by workgroup barriers; in one phase a wave
-//   issues only matrix products (PV of the previous step, then Q K^T of this
-//   step), in the other only the softmax of this step's scores. Waves 0-3 run
-//   the phases in one order and waves 4-7 in the other, so on every SIMD one
-//   wave's products overlap the other wave's softmax. Only waves 4-7 move
-//   K and V: in their softmax phase they store the next step's staged
+//   has two phases with one workgroup barrier between them; in one phase a
+//   wave issues only matrix products (PV of the previous step, then Q K^T of
+//   this step), in the other only the softmax of this step's scores. Waves
+//   0-3 run the phases in one order and waves 4-7 in the other, so on every
+//   SIMD one wave's products overlap the other wave's softmax. Only waves 4-7
+//   move K and V: in their softmax phase they store the next step's staged
 //   registers and load the step after, one chunk between blocks of
-//   exponentials, so the step top is a bare barrier and the products of
-//   waves 0-3 never wait behind load issue. Smaller workgroups
+//   exponentials, so the products of waves 0-3 never wait behind load issue;
+//   the barrier after that phase publishes the stage. Smaller workgroups
 //   have no partner wave: they run QK^T, softmax and PV in turn. 512-row
 //   query tiles run as two 256-row workgroups.
 // * Lazy rescaling: a row keeps its exponent base until its running max
