@@ -101,9 +101,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 0xffff in each half of pair j whose bit (2j, 2j+1) of bits is set.
+// 0xffff in each half of pair j whose bit (2j, 2j+1) of bits is set: each bit
+// sign-extended to a full word, the two words merged by a bitfield insert.
 __device__ __forceinline__ uint32_t pair_mask(uint32_t bits, int j) {
-    return ((bits >> (2 * j)) & 1u ? 0x0000ffffu : 0u) | ((bits >> (2 * j + 1)) & 1u ? 0xffff0000u : 0u);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * j, 1);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * j + 1, 1);
+    return (lo & 0x0000ffffu) | (hi & 0xffff0000u);
+}
+
+// Sum of the two bf16 halves of each word, accumulated in fp32 (v_dot2 with ones).
+__device__ __forceinline__ float pair_sum(const uint32_t (&w)[4], float acc) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w[j]), one, acc, false);
+    return acc;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
@@ -330,11 +342,10 @@ void route_partial_kernel(RArgs a) {
                 ht[j] = hd[j] & mt;
                 lt[j] = ld[j] & mt;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lsum[1] += ((bs >> e) & 1u) ? p[e] : 0.f;
-                lsum[2] += ((bt >> e) & 1u) ? p[e] : 0.f;
-            }
+            // masked sums from the masked high and low parts (their sum is p to
+            // about 2^-16)
+            lsum[1] = pair_sum(ls, pair_sum(hs, lsum[1]));
+            lsum[2] = pair_sum(lt, pair_sum(ht, lsum[2]));
         }
         const bf16x8 ph[3] = {as_bf16x8(hd), as_bf16x8(hs), as_bf16x8(ht)};
         const bf16x8 pl[3] = {as_bf16x8(ld), as_bf16x8(ls), as_bf16x8(lt)};
