@@ -16,12 +16,17 @@
 // (the dense running maximum, rescaled lazily), so each score costs one
 // exponential, and the masked probabilities are the dense ones with excluded
 // keys set to zero. P is split into a bf16 high part and a bf16 remainder,
-// both fed to the MFMA, so the weighted sums keep about 16 mantissa bits:
-// 7 products of 2*d FLOP per (sample, key) (one for the scores, two for each
-// softmax's output). Masks are 64-bit keep masks over the step's keys (from
-// at most two key ranges, or from the frames the step touches), a bit test
-// per score. At the end the two halves merge in LDS and the workgroup writes
-// one partial (exponent base, three sums, three unnormalised outputs) per
+// both fed to the MFMA, so the weighted sums keep about 16 mantissa bits.
+// The spatial mask keeps or drops a sample's keys a whole frame at a time:
+// when a key half is no longer than a frame (so it touches at most two
+// frames), the dense sums are kept per frame and the spatial ones formed
+// from them at the end, which leaves 5 products of 2*d FLOP per (sample,
+// key): one for the scores, two (high and low part) for the dense output,
+// two for the temporal one. Otherwise each softmax has its own sums (7
+// products). Masks are keep masks over the step's keys (from at most two
+// key ranges, or from the frames the step touches), a bit test per score.
+// At the end the two halves merge in LDS and the workgroup writes one
+// partial (exponent base, three sums, three unnormalised outputs) per
 // sample.
 // Pass 2 (route_merge_kernel): one workgroup per (sample, batch*head) merges
 // the chunk partials and forms that sample's ||o_x - o_dense||^2.
@@ -137,7 +142,7 @@ constexpr float kRouteRescaleLog2 = 8.0f;   // new base when the running max gro
 //   (keys 4 g .. 4 g + 3 and 16 + 4 g .. + 3).
 // Each lane then owns 8 (sample, key) scores per 32-key step and 3 * D / 16
 // accumulator registers, so two waves share each SIMD.
-template <int D>
+template <int D, bool TWO>
 __global__ __launch_bounds__(kRouteBlocks * kRouteParts * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void route_partial_kernel(RArgs a) {
     constexpr int KSUB = 32;
@@ -165,6 +170,13 @@ void route_partial_kernel(RArgs a) {
     const int c0 = chunk * a.chunk + part * sub;
     const int c1 = imin(N, c0 + sub);                  // keys of this half: [c0, c1), possibly empty
     const int steps = sub / KSUB;                      // the same for every wave: equal barrier counts
+    // TWO (a half no longer than a frame): the half's keys lie in frame fa and
+    // possibly fa + 1, from key kbnd on. Sum set 0 then takes the dense terms
+    // of the current frame, and when frame fa + 1 begins, frame fa's sums
+    // move to set 1; the spatial output is formed at the end from the frames
+    // the sample's mask keeps.
+    const int fa = (int)g.divS.div((uint32_t)imin(c0, N - 1));
+    const int kbnd = (fa + 1) * g.S;
     char* sm = smem + part * 2 * St::STAGE;
     const size_t head_off = (size_t)bh * N * D;
     const uint16_t* kh = a.k + head_off;
@@ -183,6 +195,8 @@ void route_partial_kernel(RArgs a) {
     uint32_t fq, sq;
     g.divS.divmod((uint32_t)qtok, fq, sq);
 
+    // unnormalised outputs and sums: dense, spatial, temporal (TWO: the
+    // current frame's dense terms, frame fa's once fa + 1 has begun, temporal)
     f32x4 oacc[3][DB];
 #pragma unroll
     for (int x = 0; x < 3; ++x)
@@ -256,8 +270,15 @@ void route_partial_kernel(RArgs a) {
         // and the temporal one the sample's window within it, or all of a sink
         // frame. A step across frames takes the general ranges.
         const int f0 = (int)g.divS.div((uint32_t)kb0);
+        const bool one_frame = f0 == (int)g.divS.div((uint32_t)(kb0 + KSUB - 1));
         uint32_t bs, bt;
-        if (f0 == (int)g.divS.div((uint32_t)(kb0 + KSUB - 1))) {
+        // TWO: frame fa + 1 begins in this step (wave-uniform); bs marks its keys of frame fa
+        const bool cross = TWO && kb0 <= kbnd && kbnd < kb0 + KSUB;
+        if constexpr (TWO) {
+            bs = cross ? mine(window_bits32(kb0, kbnd, kb0)) : 0xffu;
+            bt = one_frame ? (f0 < g.k ? 0xffu : mine(window_bits32(f0 * g.S + tlo, f0 * g.S + thi, kb0)))
+                           : mine(temporal_bits(kb0));
+        } else if (one_frame) {
             bs = f0 < g.k || abs(f0 - (int)fq) <= g.bs ? 0xffu : 0u;
             bt = f0 < g.k ? 0xffu : mine(window_bits32(f0 * g.S + tlo, f0 * g.S + thi, kb0));
         } else {
@@ -317,44 +338,102 @@ void route_partial_kernel(RArgs a) {
             ld[j] = pack_bf16(p[2 * j] - __builtin_bit_cast(float, hd[j] << 16),
                               p[2 * j + 1] - __builtin_bit_cast(float, hd[j] & 0xffff0000u));
         }
-        lsum[0] += psum;
-        // masked P^T: the dense pairs with excluded keys zeroed. Usually every lane
-        // keeps all or none of its 8 keys under each mask (a range boundary falls
-        // inside few of them): then whole pairs are selected
-        uint32_t hs[4], ls[4], ht[4], lt[4];
-        if (__all((bs == 0u || bs == 0xffu) && (bt == 0u || bt == 0xffu))) {
-            const uint32_t ms = bs ? ~0u : 0u, mt = bt ? ~0u : 0u;
+        if constexpr (TWO) {
+            // temporal P^T: the dense pairs outside the window zeroed (whole
+            // pairs when each lane keeps all or none of its 8 keys, the usual case)
+            uint32_t ht[4], lt[4];
+            if (__all(bt == 0u || bt == 0xffu)) {
+                const uint32_t mt = bt ? ~0u : 0u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hs[j] = hd[j] & ms;
-                ls[j] = ld[j] & ms;
-                ht[j] = hd[j] & mt;
-                lt[j] = ld[j] & mt;
+                for (int j = 0; j < 4; ++j) {
+                    ht[j] = hd[j] & mt;
+                    lt[j] = ld[j] & mt;
+                }
+                lsum[2] += bt ? psum : 0.f;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t mt = pair_mask(bt, j);
+                    ht[j] = hd[j] & mt;
+                    lt[j] = ld[j] & mt;
+                }
+                lsum[2] = pair_sum(lt, pair_sum(ht, lsum[2]));
             }
-            lsum[1] += bs ? psum : 0.f;
-            lsum[2] += bt ? psum : 0.f;
+            float dsum = psum;
+            if (cross) {
+                // the step where frame fa + 1 begins (once per half at most): its keys
+                // of frame fa close that frame's sums, which move to the second
+                // set; the first set restarts with the keys from kbnd on
+                uint32_t ha[4], la[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t ma = pair_mask(bs, j);
+                    ha[j] = hd[j] & ma;
+                    la[j] = ld[j] & ma;
+                    hd[j] &= ~ma;
+                    ld[j] &= ~ma;
+                }
+                const bf16x8 aph = as_bf16x8(ha), apl = as_bf16x8(la);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], aph, oacc[0][db], 0, 0, 0);
+                    oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], apl, oacc[1][db], 0, 0, 0);
+                    oacc[0][db] = f32x4{};
+                }
+                lsum[1] = pair_sum(la, pair_sum(ha, lsum[0]));
+                lsum[0] = 0.f;
+                dsum = pair_sum(ld, pair_sum(hd, 0.f));
+            }
+            // the step's dense P^T (from kbnd on, in the step where frame fa + 1 begins)
+            lsum[0] += dsum;
+            const bf16x8 dph = as_bf16x8(hd), dpl = as_bf16x8(ld), tph = as_bf16x8(ht), tpl = as_bf16x8(lt);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], dph, oacc[0][db], 0, 0, 0);
+                oacc[2][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], tph, oacc[2][db], 0, 0, 0);
+                oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], dpl, oacc[0][db], 0, 0, 0);
+                oacc[2][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], tpl, oacc[2][db], 0, 0, 0);
+            }
         } else {
+            lsum[0] += psum;
+            // masked P^T: the dense pairs with excluded keys zeroed. Usually every lane
+            // keeps all or none of its 8 keys under each mask (a range boundary falls
+            // inside few of them): then whole pairs are selected
+            uint32_t hs[4], ls[4], ht[4], lt[4];
+            if (__all((bs == 0u || bs == 0xffu) && (bt == 0u || bt == 0xffu))) {
+                const uint32_t ms = bs ? ~0u : 0u, mt = bt ? ~0u : 0u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t ms = pair_mask(bs, j), mt = pair_mask(bt, j);
-                hs[j] = hd[j] & ms;
-                ls[j] = ld[j] & ms;
-                ht[j] = hd[j] & mt;
-                lt[j] = ld[j] & mt;
+                for (int j = 0; j < 4; ++j) {
+                    hs[j] = hd[j] & ms;
+                    ls[j] = ld[j] & ms;
+                    ht[j] = hd[j] & mt;
+                    lt[j] = ld[j] & mt;
+                }
+                lsum[1] += bs ? psum : 0.f;
+                lsum[2] += bt ? psum : 0.f;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t ms = pair_mask(bs, j), mt = pair_mask(bt, j);
+                    hs[j] = hd[j] & ms;
+                    ls[j] = ld[j] & ms;
+                    ht[j] = hd[j] & mt;
+                    lt[j] = ld[j] & mt;
+                }
+                // masked sums from the masked high and low parts (their sum is p to
+                // about 2^-16)
+                lsum[1] = pair_sum(ls, pair_sum(hs, lsum[1]));
+                lsum[2] = pair_sum(lt, pair_sum(ht, lsum[2]));
             }
-            // masked sums from the masked high and low parts (their sum is p to
-            // about 2^-16)
-            lsum[1] = pair_sum(ls, pair_sum(hs, lsum[1]));
-            lsum[2] = pair_sum(lt, pair_sum(ht, lsum[2]));
-        }
-        const bf16x8 ph[3] = {as_bf16x8(hd), as_bf16x8(hs), as_bf16x8(ht)};
-        const bf16x8 pl[3] = {as_bf16x8(ld), as_bf16x8(ls), as_bf16x8(lt)};
+            const bf16x8 ph[3] = {as_bf16x8(hd), as_bf16x8(hs), as_bf16x8(ht)};
+            const bf16x8 pl[3] = {as_bf16x8(ld), as_bf16x8(ls), as_bf16x8(lt)};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+            for (int db = 0; db < DB; ++db) {
 #pragma unroll
-            for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], ph[x], oacc[x][db], 0, 0, 0);
+                for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], ph[x], oacc[x][db], 0, 0, 0);
 #pragma unroll
-            for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pl[x], oacc[x][db], 0, 0, 0);
+                for (int x = 0; x < 3; ++x) oacc[x][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pl[x], oacc[x][db], 0, 0, 0);
+            }
         }
 
         // nxt holds step s+1: to LDS, then refill it with step s+AHEAD
@@ -369,6 +448,24 @@ void route_partial_kernel(RArgs a) {
         if (s + 1 < steps) step(s + 1, st0);
     }
 
+    if constexpr (TWO) {
+        // sums of frame fa: the second set if frame fa + 1 began in the half,
+        // else the first. Dense = both sets (the second is zero when unused);
+        // spatial = the frames the sample's mask keeps.
+        const bool crossed = c0 <= kbnd && kbnd < c0 + sub;
+        const bool ka = fa < g.k || abs(fa - (int)fq) <= g.bs;
+        const bool kb = fa + 1 < g.k || abs(fa + 1 - (int)fq) <= g.bs;
+        const bool keep1 = crossed ? ka : false, keep0 = crossed ? kb : ka;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4 o0 = oacc[0][db], o1 = oacc[1][db];
+            oacc[0][db] = o0 + o1;
+            oacc[1][db] = keep0 ? (keep1 ? o0 + o1 : o0) : (keep1 ? o1 : f32x4{});
+        }
+        const float l0 = lsum[0], l1 = lsum[1];
+        lsum[0] = l0 + l1;
+        lsum[1] = keep0 ? (keep1 ? l0 + l1 : l0) : (keep1 ? l1 : 0.f);
+    }
     // ---- the two key halves of each sample block merge in LDS; half 0 writes the partial
     float lt3[3];
 #pragma unroll
@@ -514,8 +611,13 @@ __global__ void route_flag_kernel(RArgs a, int BH) {
 
 template <int D>
 hipError_t launch_pair(const RArgs& r, int BH, hipStream_t stream) {
-    hipLaunchKernelGGL((route_partial_kernel<D>), dim3(r.n_chunks, BH), dim3(kRouteBlocks * kRouteParts * 64), 0,
-                       stream, r);
+    // per-frame dense sums when a key half (chunk / 2 keys) fits in a frame
+    if (r.chunk / kRouteParts <= r.g.S)
+        hipLaunchKernelGGL((route_partial_kernel<D, true>), dim3(r.n_chunks, BH), dim3(kRouteBlocks * kRouteParts * 64),
+                           0, stream, r);
+    else
+        hipLaunchKernelGGL((route_partial_kernel<D, false>), dim3(r.n_chunks, BH), dim3(kRouteBlocks * kRouteParts * 64),
+                           0, stream, r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_merge_kernel<D>), dim3(r.ns, BH), dim3(D), 0, stream, r);

@@ -495,6 +495,26 @@ def test_routing_finds_planted_kinds(dev):
     assert tuple(f[0]) == kinds and tuple(f_ref[0]) == kinds
 
 
+@pytest.mark.parametrize("geom,d,mask", [
+    ((8, 7, 11), 64, (1, 1, 9, 0)),    # S = 77: frame boundaries inside 32-key steps; the last half ends past N
+    ((8, 7, 11), 128, (2, 2, 30, 0)),
+    ((6, 8, 12), 128, (1, 1, 20, 0)),  # S = 96: a frame boundary on a step's first key
+    ((6, 8, 12), 64, (0, 0, 5, 0)),
+])
+def test_routing_frame_boundaries_inside_key_halves(dev, geom, d, mask):
+    """Key halves of 64 keys that reach into a second frame: the kernel sums
+    the dense output per frame and forms the spatial one from the frames a
+    sample keeps, so a boundary inside a step, on a step's first key and at
+    the end of the sequence must all match the oracle."""
+    F, H, W = geom
+    N = F * H * W
+    say(f"routing frame boundaries geom={geom} d={d} mask={mask}")
+    for n, seed in ((64, 11), (5, 12)):
+        q, k, v = normal_qkv(1, 2, N, d, seed=seed)
+        idx = sample_indices(N, n, seed=seed).numpy()
+        check_routing(dev, geom, mask, q * 3, k, v, idx)
+
+
 def test_routing_head_dim_128_ragged_chunks(dev):
     geom = (5, 7, 9)          # 315 tokens: chunks end mid-tile
     mask = (1, 1, 4, 0)
