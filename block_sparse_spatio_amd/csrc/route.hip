@@ -212,12 +212,14 @@ void route_partial_kernel(RArgs a) {
     constexpr int AHEAD = DEEP ? 3 : 2;
     St st0, st1;
     auto ident = [](int j) { return j; };
-    if (steps > 0) {
-        st0.load(kh, vh, c0, N, ident, ptid);
-        st0.store(sm, ptid);
-        if (steps > 1) (DEEP ? st1 : st0).load(kh, vh, c0 + KSUB, N, ident, ptid);
-        if (DEEP && steps > 2) st0.load(kh, vh, c0 + 2 * KSUB, N, ident, ptid);
-    }
+    // A chunk is a multiple of 128 keys, so every half has at least 2 steps.
+    // No branch around these first copies: the wait for their loads then also
+    // covers the Q loads on every path into the loop, so the loop's products
+    // on Q carry no wait for the loads in flight.
+    st0.load(kh, vh, c0, N, ident, ptid);
+    st0.store(sm, ptid);
+    (DEEP ? st1 : st0).load(kh, vh, c0 + KSUB, N, ident, ptid);
+    if (DEEP && steps > 2) st0.load(kh, vh, c0 + 2 * KSUB, N, ident, ptid);
     __syncthreads();
 
     // temporal keep mask over the 32 keys base .. base+31: sink frames whole,
