@@ -496,22 +496,31 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
             __builtin_amdgcn_sched_barrier(0);
         };
         auto top = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
-        // gathered rows: the source rows of the keys that step s's transfer loads,
-        // found in the matrix phase before it (where VALU time is free): lane i
-        // finds the source of key kb + i, each chunk takes its row's from that lane
-        int srow[Sh::CU];
+        // buffer offsets of the rows that step s's transfer loads, found in the
+        // matrix phase before it (where VALU time is free), so that the vector
+        // phase only issues the loads; gathered rows: lane i finds the source
+        // of key kb + i and each chunk takes its row's from that lane. The LDS
+        // side stores at one per-thread base per tensor plus constant offsets.
+        int loff[Sh::CU];
         auto prep = [&](int s) __attribute__((always_inline)) {
             if constexpr (GATHER) {
                 const int my = next_keys(s) + lane;
                 const int mysrc = lane < KSUB && my < N ? (gat ? temporal_src(g, my) : my) : -1;
 #pragma unroll
-                for (int r = 0; r < Sh::CU; ++r) srow[r] = __shfl(mysrc, Sh::chunk_row(r, htid));
+                for (int r = 0; r < Sh::CU; ++r) loff[r] = Sh::chunk_off(r, htid, __shfl(mysrc, Sh::chunk_row(r, htid)));
+            } else {
+                const int kb = next_keys(s);
+#pragma unroll
+                for (int r = 0; r < Sh::CU; ++r) {
+                    const int j = kb + Sh::chunk_row(r, htid);
+                    loff[r] = Sh::chunk_off(r, htid, j < N ? j : -1);
+                }
             }
         };
+        const int kl0 = Sh::k_off(htid / Sh::RV, htid % Sh::RV), vl0 = Sh::v_off(htid / Sh::RV, htid % Sh::RV);
         // softmax of step t; with XFER (waves 4-7, step s) the stage transfer rides along
         auto soft = [&](auto masked, auto xfer, int t, int s) __attribute__((always_inline)) {
             char* dst = wstage(s + 1);
-            const int kb = decltype(xfer)::value ? next_keys(s) : 0;
 
             // chunk r goes with hook point r * NH / CU (NH = KSUB / 16 points)
             auto hook = [&](int k) __attribute__((always_inline)) {
@@ -521,11 +530,8 @@ __device__ __forceinline__ void attn_item(const KArgs& a, const int logical, con
                     for (int r = 0; r < Sh::CU; ++r) {
                         if (r * NH / Sh::CU != k) continue;
                         __builtin_amdgcn_sched_barrier(0);
-                        sh.store_chunk(r, dst, htid);
-                        if constexpr (GATHER)
-                            sh.load_chunk_at(r, rsk, rsv, srow[r], htid);
-                        else
-                            sh.load_chunk(r, rsk, rsv, kb, N, src, htid);
+                        sh.store_chunk_at(r, dst + kl0, dst + vl0);
+                        sh.load_chunk_off(r, rsk, rsv, loff[r]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }

@@ -87,42 +87,28 @@ struct Stager {
         }
     }
 
-    // Chunk r of load() alone, through buffer loads and without a branch: a
-    // row at or past limit gets an offset beyond the buffer's end, which the
-    // hardware reads as zero. rk / rv cover one head's K / V rows.
-    template <class Src>
-    __device__ __forceinline__ void load_chunk(int r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int kb0,
-                                               int limit, Src src, int tid) {
-        const int u = tid + r * NT;
-        const int row = u / RV, c = u % RV;
-        const int j = kb0 + row;
-        const int off = j < limit ? src(j) * (D * 2) + c * 16 : 0x7ffffff0;
+    // Byte offset in the K / V buffers of chunk r of thread tid for source row
+    // j; j < 0 gives an offset beyond the buffer's end, which buffer loads
+    // read as zero (no branch around the load).
+    __device__ __forceinline__ static int chunk_off(int r, int tid, int j) {
+        const int c = (tid + r * NT) % RV;
+        return j >= 0 ? j * (D * 2) + c * 16 : 0x7ffffff0;
+    }
+    // Chunk r of load() at a byte offset found by chunk_off.
+    __device__ __forceinline__ void load_chunk_off(int r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int off) {
         kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
         vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
-
-    // Chunk r of load() from source row srow (negative: read as zero), the
-    // row found by the caller.
-    __device__ __forceinline__ void load_chunk_at(int r, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                                  int srow, int tid) {
-        const int u = tid + r * NT;
-        const int c = u % RV;
-        const int off = srow >= 0 ? srow * (D * 2) + c * 16 : 0x7ffffff0;
-        kreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-        vreg[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    // Chunk r of store() from the thread's chunk-0 addresses kl = stage +
+    // k_off(row0, c), vl = stage + v_off(row0, c): chunk r is NT / RV rows on.
+    __device__ __forceinline__ void store_chunk_at(int r, char* kl, char* vl) const {
+        static_assert(NT % RV == 0, "chunks of one thread share a column");
+        *reinterpret_cast<uint4*>(kl + r * (NT / RV) * KROW) = kreg[r];
+        *reinterpret_cast<uint4*>(vl + r * (NT / RV) * VROW) = vreg[r];
     }
 
     // Row of the sub-tile that chunk r of thread tid holds.
     __device__ __forceinline__ static int chunk_row(int r, int tid) { return (tid + r * NT) / RV; }
-
-    // Chunk r of store() alone (CH a multiple of NT).
-    __device__ __forceinline__ void store_chunk(int r, char* stage, int tid) const {
-        static_assert(CH % NT == 0, "every thread owns CU chunks");
-        const int u = tid + r * NT;
-        const int row = u / RV, c = u % RV;
-        *reinterpret_cast<uint4*>(stage + k_off(row, c)) = kreg[r];
-        *reinterpret_cast<uint4*>(stage + v_off(row, c)) = vreg[r];
-    }
 
     __device__ __forceinline__ void store(char* stage, int tid) const {
 #pragma unroll
