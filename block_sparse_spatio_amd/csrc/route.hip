@@ -600,15 +600,24 @@ __global__ __launch_bounds__(D) void route_merge_kernel(RArgs a) {
     }
 }
 
-// One thread per batch*head: sum the per-sample deviations in sample order, set the flag.
-__global__ void route_flag_kernel(RArgs a, int BH) {
+// One thread per batch*head: sum the per-sample deviations in sample order,
+// set the flag. All kMaxSamples pairs are loaded first (the workspace holds
+// them for every head; slots past n_samples are never used), so the loads
+// overlap instead of forming a chain.
+__global__ __launch_bounds__(64) void route_flag_kernel(RArgs a, int BH) {
     const int bh = blockIdx.x * blockDim.x + threadIdx.x;
     if (bh >= BH) return;
+    const float2* e2 = reinterpret_cast<const float2*>(a.ws_err + (size_t)bh * kMaxSamples * 2);
+    float2 v[kMaxSamples];
+#pragma unroll
+    for (int n = 0; n < kMaxSamples; ++n) v[n] = e2[n];
     float es = 0.f, et = 0.f;
-    for (int n = 0; n < a.ns; ++n) {
-        es += a.ws_err[((size_t)bh * kMaxSamples + n) * 2];
-        et += a.ws_err[((size_t)bh * kMaxSamples + n) * 2 + 1];
-    }
+#pragma unroll
+    for (int n = 0; n < kMaxSamples; ++n)
+        if (n < a.ns) {
+            es += v[n].x;
+            et += v[n].y;
+        }
     a.flags[bh] = et < es ? 1 : 0;
     if (a.err) {
         a.err[2 * bh] = es;
