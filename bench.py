@@ -33,7 +33,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--bq", type=int, default=256)
     ap.add_argument("--bkv", type=int, default=128)
     ap.add_argument("--mode", default="exact")
