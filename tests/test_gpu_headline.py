@@ -310,6 +310,31 @@ def test_headline_whole_query_tiles(dev, headline):
         assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
 
 
+def test_headline_routing(dev):
+    """Routing at 75,600 tokens in the launch the benchmark times: key halves of 1,536 keys
+    in frames of 3,600, so frame boundaries fall inside 32-key steps (per-frame dense sums,
+    sets moved mid-step). Errors of spatial and temporal heads against the oracle within
+    1e-3 of the larger, flags equal, and the planted kinds found."""
+    w = HEADLINE
+    geom, mask = geom_mask(w)
+    say("headline routing inputs")
+    q, k, v = planted_qkv(1, w.F, w.H, w.W, w.d, w.kinds, seed=3)
+    idx = sample_indices(w.N, 64, seed=3)
+    flags, err = B.svga_route_heads(q.to(dev), k.to(dev), v.to(dev), geom, mask, idx.to(dev))
+    f = flags.cpu().numpy()
+    e = err.cpu().numpy()
+    say(f"  flags {f.tolist()}")
+    assert tuple(f[0]) == w.kinds
+    scale = 1 / math.sqrt(w.d)
+    for h in (0, 4, 5, 9):
+        fr, er = O.route_heads(q[:, h:h + 1].double().numpy(), k[:, h:h + 1].double().numpy(),
+                               v[:, h:h + 1].double().numpy(), w.F, w.H, w.W, *mask[:3], idx.numpy(), scale)
+        rel = np.abs(e[0, h] - er[0, 0]).max() / er[0, 0].max()
+        say(f"  head {h}: gpu err {e[0, h].tolist()} oracle {er[0, 0].tolist()} relative {rel:.2e}")
+        assert rel <= 1e-3
+        assert f[0, h] == fr[0, 0]
+
+
 def test_1440p_routing_and_attention(dev):
     """Routing on 64 sampled queries at 302,400 tokens finds the planted head kinds; the routed
     pipeline matches the oracle on sampled rows."""
