@@ -6,6 +6,7 @@
 rows one by one (each row's softmax over all 75,600 or 302,400 keys), plus
 every row of the first and last query tiles.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -123,6 +124,36 @@ def test_headline_sampled_rows(dev, headline, mode, bq):
         say(f"  head {h} kind {kind}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
             f"(|ref| max {np.abs(ref).max():.3f}); LSE max err {lerr.max():.2e}")
         assert np.isfinite(got).all()
+        assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
+        assert lerr.max() < 1e-3
+
+
+@pytest.mark.parametrize("bq", [256, 128])
+def test_headline_head_dim_64(dev, bq):
+    """The headline shape at head dim 64 (its own kernel instances: the 8-wave ping-pong at 256
+    rows, the 4-wave kernel at 128) in the persistent split-tail launch: output and LSE against
+    the oracle on sampled rows, and the in-kernel gather bitwise equal to the permuted path."""
+    w = dataclasses.replace(HEADLINE, d=64)
+    geom, mask = geom_mask(w)
+    q, k, v = normal_qkv(1, w.heads, w.N, w.d, seed=5)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    flags = torch.tensor([w.kinds], dtype=torch.uint8, device=dev)
+    say(f"headline d=64 bq={bq}")
+    o, lse = pipeline(dev, w, qd, kd, vd, flags, bq, 128, B.MAP_EXACT, workspace=split_workspace(dev, w, bq),
+                      want_lse=True)
+    og = pipeline(dev, w, qd, kd, vd, flags, bq, 128, B.MAP_EXACT, gather=True, workspace=split_workspace(dev, w, bq))
+    assert torch.equal(o.view(torch.int16), og.view(torch.int16))
+    o, lse = o.cpu(), lse.cpu()
+    scale = 1 / math.sqrt(w.d)
+    for h in (0, 4, 5, 9):
+        kind = w.kinds[h]
+        rows = sample_rows(w.N, bq, 64, seed=10 + h)
+        ref, ref_lse = O.attention_head(q[0, h].double().numpy(), k[0, h].double().numpy(), v[0, h].double().numpy(),
+                                        kind, w.F, w.H, w.W, *mask[:3], mask[3], B.MAP_EXACT, bq, 128, scale,
+                                        rows=rows)
+        err = np.abs(o[0, h, rows].double().numpy() - ref)
+        lerr = np.abs(lse[0, h, rows].double().numpy() - ref_lse)
+        say(f"  head {h} kind {kind}: max-abs {err.max():.3e} mean-abs {err.mean():.3e}; LSE max err {lerr.max():.2e}")
         assert err.max() < MAX_ABS and err.mean() < MEAN_ABS
         assert lerr.max() < 1e-3
 
