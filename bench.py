@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--mode", default="exact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the variant and sweep timings")
+    ap.add_argument("--layer-1440p", action="store_true",
+                    help="only time the 302,400-token layer (routing, tile map, permutations, attention, "
+                         "unpermutation) and print its figures as one JSON line (for kernel traces)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--cpu-full", action="store_true",
                     help="time the oracle on whole heads and the whole tile map, routing and permutations "
@@ -61,6 +64,10 @@ def main():
 
     w = HEADLINE
     dev = torch.device("cuda:0")
+    if args.layer_1440p:
+        aws = torch.empty(B.svga_attn_split_workspace_bytes(P1440.d, 512), dtype=torch.uint8, device=dev)
+        print(json.dumps(layer_1440p(B, torch, dev, P1440, aws)), flush=True)
+        return
     geom = (w.F, w.H, w.W)
     mask = (w.sink_frames, w.spatial_band, w.temporal_band, w.temporal_layout)
     mode = B.MODES[args.mode]
